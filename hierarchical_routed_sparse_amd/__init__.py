@@ -1,0 +1,277 @@
+"""MI355X (gfx950) Hierarchical Global Attention: Python binding of libhga.so.
+
+The functions below carry the names of the C ABI in ``include/hga.h`` and do
+argument marshalling only (shape struct, device pointers, current HIP stream);
+every step of the method runs in the library's HIP kernels.  Torch is used for
+device memory and streams.  If ``libhga.so`` has not been built, the first call
+raises ``HGAError``: there is no fallback implementation.
+
+Tensors: Q, O, dO, dQ [B,Hq,q_len,D]; K, V, dK, dV [B,Hkv,kv_len,D] of the
+shape's dtype (torch.bfloat16 or torch.float32); chunk_mean
+[B,Hkv,kv_len/64,D] and group_mean [B,Hkv,kv_len/8,D] float32; chunk_idx
+[B,Hq,q_len/64,top_k] and group_idx [B,Hq,q_len/64,top_g] int32; lse
+[B,Hq,q_len] float32.  All contiguous, on the current GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "HGAError", "HgaShape", "make_shape", "lib_path", "hga_abi_version", "hga_validate_shape",
+    "hga_build_summaries", "hga_route", "hga_attend_fwd", "hga_attend_bwd_workspace",
+    "hga_attend_bwd", "hga_attend_bwd_dq", "hga_attend_bwd_dkdv", "forward", "backward",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhga.so")
+
+HGA_DTYPE_BF16, HGA_DTYPE_FP32 = 0, 1
+CHUNK, GROUP, QBLOCK = 64, 8, 64
+
+
+class HGAError(RuntimeError):
+    pass
+
+
+class HgaShape(ctypes.Structure):
+    """Mirror of ``hga_shape`` in include/hga.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("q_len", ctypes.c_int32), ("kv_len", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("top_g", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+    ]
+
+    def __repr__(self):
+        f = ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_)
+        return f"HgaShape({f})"
+
+
+def make_shape(batch, n_q_heads, n_kv_heads, head_dim, q_len, kv_len, top_k, top_g,
+               dtype="bf16", softmax_scale=0.0) -> HgaShape:
+    dt = {"bf16": HGA_DTYPE_BF16, "fp32": HGA_DTYPE_FP32}.get(dtype, dtype)
+    return HgaShape(batch, n_q_heads, n_kv_heads, head_dim, q_len, kv_len, top_k, top_g,
+                    float(softmax_scale), int(dt))
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_SP = ctypes.POINTER(HgaShape)
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise HGAError(f"{LIB_PATH} is not built; run python -m hierarchical_routed_sparse_amd.build_lib")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, sz = ctypes.c_int32, ctypes.c_size_t
+    lib.hga_abi_version.restype = ctypes.c_int
+    lib.hga_status_str.restype = ctypes.c_char_p
+    lib.hga_status_str.argtypes = [ctypes.c_int]
+    lib.hga_validate_shape.argtypes = [_SP]
+    lib.hga_build_summaries.argtypes = [_SP, _vp, _vp, _vp, i32, i32, _vp]
+    lib.hga_route.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.hga_attend_fwd.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.hga_attend_bwd_workspace.argtypes = [_SP, ctypes.POINTER(sz)]
+    lib.hga_attend_bwd.argtypes = [_SP] + [_vp] * 11 + [sz, _vp]
+    lib.hga_attend_bwd_dq.argtypes = [_SP] + [_vp] * 9 + [sz, _vp]
+    lib.hga_attend_bwd_dkdv.argtypes = [_SP] + [_vp] * 9 + [sz, _vp]
+    for name in ("hga_validate_shape", "hga_build_summaries", "hga_route", "hga_attend_fwd",
+                 "hga_attend_bwd_workspace", "hga_attend_bwd", "hga_attend_bwd_dq",
+                 "hga_attend_bwd_dkdv"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise HGAError(f"{what}: {_load().hga_status_str(rc).decode()} (status {rc})")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _elt_dtype(shape: HgaShape):
+    import torch
+    return torch.bfloat16 if shape.dtype == HGA_DTYPE_BF16 else torch.float32
+
+
+def _ptr(t, name, dtype=None, size=None, nullable=False):
+    """Device pointer of a contiguous tensor after checking dtype and shape."""
+    if t is None:
+        if nullable:
+            return None
+        raise HGAError(f"{name} is required")
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise HGAError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise HGAError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise HGAError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if size is not None and tuple(t.shape) != tuple(size):
+        raise HGAError(f"{name} has shape {tuple(t.shape)}, expected {tuple(size)}")
+    return t.data_ptr()
+
+
+def _sizes(s: HgaShape):
+    nblk = s.q_len // QBLOCK
+    return dict(
+        q=(s.batch, s.n_q_heads, s.q_len, s.head_dim),
+        kv=(s.batch, s.n_kv_heads, s.kv_len, s.head_dim),
+        cm=(s.batch, s.n_kv_heads, s.kv_len // CHUNK, s.head_dim),
+        gm=(s.batch, s.n_kv_heads, s.kv_len // GROUP, s.head_dim),
+        ci=(s.batch, s.n_q_heads, nblk, s.top_k),
+        gi=(s.batch, s.n_q_heads, nblk, s.top_g),
+        lse=(s.batch, s.n_q_heads, s.q_len),
+    )
+
+
+# ------------------------------------------------------------------ C ABI names
+
+def hga_abi_version() -> int:
+    return _load().hga_abi_version()
+
+
+def hga_validate_shape(shape: HgaShape) -> int:
+    """Returns the status code (0 = valid); host only."""
+    return _load().hga_validate_shape(ctypes.byref(shape))
+
+
+def hga_build_summaries(shape, K, chunk_mean, group_mean, chunk_begin=0, chunk_end=None,
+                        stream=None):
+    import torch
+    sz = _sizes(shape)
+    if chunk_end is None:
+        chunk_end = shape.kv_len // CHUNK
+    _check(_load().hga_build_summaries(
+        ctypes.byref(shape), _ptr(K, "K", _elt_dtype(shape), sz["kv"]),
+        _ptr(chunk_mean, "chunk_mean", torch.float32, sz["cm"]),
+        _ptr(group_mean, "group_mean", torch.float32, sz["gm"]),
+        int(chunk_begin), int(chunk_end), _stream(stream)), "hga_build_summaries")
+
+
+def hga_route(shape, Q, chunk_mean, group_mean, chunk_idx, group_idx, stream=None):
+    import torch
+    sz = _sizes(shape)
+    _check(_load().hga_route(
+        ctypes.byref(shape), _ptr(Q, "Q", _elt_dtype(shape), sz["q"]),
+        _ptr(chunk_mean, "chunk_mean", torch.float32, sz["cm"]),
+        _ptr(group_mean, "group_mean", torch.float32, sz["gm"], nullable=True),
+        _ptr(chunk_idx, "chunk_idx", torch.int32, sz["ci"], nullable=True),
+        _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        _stream(stream)), "hga_route")
+
+
+def hga_attend_fwd(shape, Q, K, V, group_idx, O, lse=None, stream=None):
+    import torch
+    sz, dt = _sizes(shape), _elt_dtype(shape)
+    _check(_load().hga_attend_fwd(
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"]),
+        _ptr(V, "V", dt, sz["kv"]),
+        _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        _ptr(O, "O", dt, sz["q"]), _ptr(lse, "lse", torch.float32, sz["lse"], nullable=True),
+        _stream(stream)), "hga_attend_fwd")
+
+
+def hga_attend_bwd_workspace(shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_load().hga_attend_bwd_workspace(ctypes.byref(shape), ctypes.byref(n)),
+           "hga_attend_bwd_workspace")
+    return int(n.value)
+
+
+def _ws(workspace):
+    if isinstance(workspace, int):
+        raise HGAError("pass the workspace as a tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def hga_attend_bwd(shape, Q, K, V, O, lse, dO, group_idx, dQ, dK, dV, workspace, stream=None):
+    import torch
+    sz, dt = _sizes(shape), _elt_dtype(shape)
+    wp, wb = _ws(workspace)
+    _check(_load().hga_attend_bwd(
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"]),
+        _ptr(V, "V", dt, sz["kv"]), _ptr(O, "O", dt, sz["q"]),
+        _ptr(lse, "lse", torch.float32, sz["lse"]), _ptr(dO, "dO", dt, sz["q"]),
+        _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        _ptr(dQ, "dQ", dt, sz["q"]), _ptr(dK, "dK", dt, sz["kv"]), _ptr(dV, "dV", dt, sz["kv"]),
+        wp, wb, _stream(stream)), "hga_attend_bwd")
+
+
+def hga_attend_bwd_dq(shape, Q, K, V, O, lse, dO, group_idx, dQ, workspace, stream=None):
+    import torch
+    sz, dt = _sizes(shape), _elt_dtype(shape)
+    wp, wb = _ws(workspace)
+    _check(_load().hga_attend_bwd_dq(
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"]),
+        _ptr(V, "V", dt, sz["kv"]), _ptr(O, "O", dt, sz["q"]),
+        _ptr(lse, "lse", torch.float32, sz["lse"]), _ptr(dO, "dO", dt, sz["q"]),
+        _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        _ptr(dQ, "dQ", dt, sz["q"]), wp, wb, _stream(stream)), "hga_attend_bwd_dq")
+
+
+def hga_attend_bwd_dkdv(shape, Q, K, V, lse, dO, group_idx, dK, dV, workspace, stream=None):
+    import torch
+    sz, dt = _sizes(shape), _elt_dtype(shape)
+    wp, wb = _ws(workspace)
+    _check(_load().hga_attend_bwd_dkdv(
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"]),
+        _ptr(V, "V", dt, sz["kv"]), _ptr(lse, "lse", torch.float32, sz["lse"]),
+        _ptr(dO, "dO", dt, sz["q"]),
+        _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        _ptr(dK, "dK", dt, sz["kv"]), _ptr(dV, "dV", dt, sz["kv"]), wp, wb, _stream(stream)),
+        "hga_attend_bwd_dkdv")
+
+
+# ------------------------------------------------------------------ compositions
+
+def forward(shape, Q, K, V, stream=None):
+    """Summaries, routing and attention with freshly allocated outputs.
+    Returns dict(chunk_mean, group_mean, chunk_idx, group_idx, O, lse)."""
+    import torch
+    sz = _sizes(shape)
+    dev = Q.device
+    out = dict(
+        chunk_mean=torch.empty(sz["cm"], dtype=torch.float32, device=dev),
+        group_mean=torch.empty(sz["gm"], dtype=torch.float32, device=dev),
+        chunk_idx=torch.empty(sz["ci"], dtype=torch.int32, device=dev),
+        group_idx=torch.empty(sz["gi"], dtype=torch.int32, device=dev),
+        O=torch.empty(sz["q"], dtype=_elt_dtype(shape), device=dev),
+        lse=torch.empty(sz["lse"], dtype=torch.float32, device=dev),
+    )
+    hga_build_summaries(shape, K, out["chunk_mean"], out["group_mean"], stream=stream)
+    hga_route(shape, Q, out["chunk_mean"], out["group_mean"], out["chunk_idx"],
+              out["group_idx"], stream=stream)
+    hga_attend_fwd(shape, Q, K, V, out["group_idx"], out["O"], out["lse"], stream=stream)
+    return out
+
+
+def backward(shape, Q, K, V, O, lse, dO, group_idx, stream=None):
+    """dQ, dK, dV with freshly allocated outputs and workspace."""
+    import torch
+    sz = _sizes(shape)
+    dev = Q.device
+    dQ = torch.empty(sz["q"], dtype=_elt_dtype(shape), device=dev)
+    dK = torch.empty(sz["kv"], dtype=_elt_dtype(shape), device=dev)
+    dV = torch.empty(sz["kv"], dtype=_elt_dtype(shape), device=dev)
+    ws = torch.empty(hga_attend_bwd_workspace(shape), dtype=torch.uint8, device=dev)
+    hga_attend_bwd(shape, Q, K, V, O, lse, dO, group_idx, dQ, dK, dV, ws, stream=stream)
+    return dQ, dK, dV

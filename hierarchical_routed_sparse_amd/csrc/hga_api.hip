@@ -1,0 +1,163 @@
+// C ABI of the HGA library: argument validation and kernel dispatch.
+// The contract of every entry point is documented in include/hga.h.
+#include "../../include/hga.h"
+
+#include <math.h>
+
+#include "hga_kernels.h"
+
+namespace {
+
+hga::Dims dims_of(const hga_shape* s) {
+  hga::Dims d;
+  d.B = s->batch;
+  d.Hq = s->n_q_heads;
+  d.Hkv = s->n_kv_heads;
+  d.D = s->head_dim;
+  d.Sq = s->q_len;
+  d.Skv = s->kv_len;
+  d.top_k = s->top_k;
+  d.top_g = s->top_g;
+  d.q0 = s->kv_len - s->q_len;
+  d.nblk = s->q_len / HGA_QBLOCK;
+  d.scale = s->softmax_scale > 0.f ? s->softmax_scale : 1.0f / sqrtf((float)s->head_dim);
+  d.bf16 = s->dtype == HGA_DTYPE_BF16;
+  return d;
+}
+
+hga_status from_hip(hipError_t e) { return e == hipSuccess ? HGA_OK : HGA_ERR_HIP; }
+
+size_t delta_bytes(const hga_shape* s) {
+  const size_t n = (size_t)s->batch * s->n_q_heads * s->q_len * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hga_abi_version(void) { return HGA_ABI_VERSION; }
+
+const char* hga_status_str(hga_status s) {
+  switch (s) {
+    case HGA_OK: return "ok";
+    case HGA_ERR_NULL: return "a required pointer is NULL";
+    case HGA_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case HGA_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
+    case HGA_ERR_WORKSPACE: return "workspace missing or too small";
+    case HGA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+hga_status hga_validate_shape(const hga_shape* s) {
+  if (!s) return HGA_ERR_NULL;
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1) return HGA_ERR_SHAPE;
+  if (s->n_q_heads % s->n_kv_heads != 0) return HGA_ERR_SHAPE;
+  if (s->q_len < HGA_QBLOCK || s->q_len % HGA_QBLOCK != 0) return HGA_ERR_SHAPE;
+  if (s->kv_len % HGA_CHUNK != 0 || s->kv_len < s->q_len || s->kv_len > HGA_MAX_KV_LEN)
+    return HGA_ERR_SHAPE;
+  if (s->top_k < 0 || s->top_k > HGA_MAX_TOP_K) return HGA_ERR_SHAPE;
+  if (s->top_g < 0 || s->top_g > HGA_MAX_TOP_G) return HGA_ERR_SHAPE;
+  if (!(s->softmax_scale == s->softmax_scale)) return HGA_ERR_SHAPE;   // NaN
+  if (s->head_dim != 64 && s->head_dim != 128) return HGA_ERR_UNSUPPORTED;
+  if (s->dtype != HGA_DTYPE_BF16 && s->dtype != HGA_DTYPE_FP32) return HGA_ERR_UNSUPPORTED;
+  // launch sizes must fit a 32-bit grid
+  const long long rows = (long long)s->batch * s->n_q_heads * (s->q_len / HGA_QBLOCK);
+  const long long chunks = (long long)s->batch * s->n_kv_heads * (s->kv_len / HGA_CHUNK);
+  if (rows > (1LL << 30) || chunks > (1LL << 30)) return HGA_ERR_SHAPE;
+  // routing rows of one kv head must fit the 23-bit row field of the backward entry list
+  if ((long long)(s->n_q_heads / s->n_kv_heads) * (s->q_len / HGA_QBLOCK) >= (1LL << 23))
+    return HGA_ERR_SHAPE;
+  return HGA_OK;
+}
+
+hga_status hga_build_summaries(const hga_shape* shape, const void* K, float* chunk_mean,
+                               float* group_mean, int32_t chunk_begin, int32_t chunk_end,
+                               void* stream) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!K || !chunk_mean || !group_mean) return HGA_ERR_NULL;
+  if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > shape->kv_len / HGA_CHUNK)
+    return HGA_ERR_SHAPE;
+  if (chunk_end == chunk_begin) return HGA_OK;
+  return from_hip(hga::launch_summaries(dims_of(shape), K, chunk_mean, group_mean, chunk_begin,
+                                        chunk_end, (hipStream_t)stream));
+}
+
+hga_status hga_route(const hga_shape* shape, const void* Q, const float* chunk_mean,
+                     const float* group_mean, int32_t* chunk_idx, int32_t* group_idx,
+                     void* stream) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!Q || !chunk_mean) return HGA_ERR_NULL;
+  if (shape->top_g > 0 && (!group_idx || !group_mean)) return HGA_ERR_NULL;
+  if (shape->top_k == 0 && shape->top_g == 0 && !group_idx && !chunk_idx) return HGA_OK;
+  return from_hip(hga::launch_route(dims_of(shape), Q, chunk_mean, group_mean,
+                                    shape->top_k > 0 ? chunk_idx : nullptr,
+                                    shape->top_g > 0 ? group_idx : nullptr,
+                                    (hipStream_t)stream));
+}
+
+hga_status hga_attend_fwd(const hga_shape* shape, const void* Q, const void* K, const void* V,
+                          const int32_t* group_idx, void* O, float* lse, void* stream) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!Q || !K || !V || !O) return HGA_ERR_NULL;
+  if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
+  return from_hip(hga::launch_attend_fwd(dims_of(shape), Q, K, V, group_idx, O, lse,
+                                         (hipStream_t)stream));
+}
+
+hga_status hga_attend_bwd_workspace(const hga_shape* shape, size_t* bytes) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!bytes) return HGA_ERR_NULL;
+  *bytes = delta_bytes(shape);
+  return HGA_OK;
+}
+
+hga_status hga_attend_bwd_dq(const hga_shape* shape, const void* Q, const void* K,
+                             const void* V, const void* O, const float* lse, const void* dO,
+                             const int32_t* group_idx, void* dQ, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!Q || !K || !V || !O || !lse || !dO || !dQ) return HGA_ERR_NULL;
+  if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
+  if (!workspace || workspace_bytes < delta_bytes(shape)) return HGA_ERR_WORKSPACE;
+  return from_hip(hga::launch_attend_bwd_dq(dims_of(shape), Q, K, V, O, lse, dO, group_idx, dQ,
+                                            (float*)workspace, (hipStream_t)stream));
+}
+
+hga_status hga_attend_bwd_dkdv(const hga_shape* shape, const void* Q, const void* K,
+                               const void* V, const float* lse, const void* dO,
+                               const int32_t* group_idx, void* dK, void* dV,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!Q || !K || !V || !lse || !dO || !dK || !dV) return HGA_ERR_NULL;
+  if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
+  if (!workspace || workspace_bytes < delta_bytes(shape)) return HGA_ERR_WORKSPACE;
+  return from_hip(hga::launch_attend_bwd_dkdv(dims_of(shape), Q, K, V, lse, dO, group_idx,
+                                              (const float*)workspace, dK, dV,
+                                              (hipStream_t)stream));
+}
+
+hga_status hga_attend_bwd(const hga_shape* shape, const void* Q, const void* K, const void* V,
+                          const void* O, const float* lse, const void* dO,
+                          const int32_t* group_idx, void* dQ, void* dK, void* dV,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!Q || !K || !V || !O || !lse || !dO || !dQ || !dK || !dV) return HGA_ERR_NULL;
+  if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
+  if (!workspace || workspace_bytes < delta_bytes(shape)) return HGA_ERR_WORKSPACE;
+  st = hga_attend_bwd_dq(shape, Q, K, V, O, lse, dO, group_idx, dQ, workspace, workspace_bytes,
+                         stream);
+  if (st != HGA_OK) return st;
+  return hga_attend_bwd_dkdv(shape, Q, K, V, lse, dO, group_idx, dK, dV, workspace,
+                             workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,37 @@
+// Internal launch interface between the C ABI (hga_api.hip) and the kernels.
+// Shapes have been validated by the caller; every function only enqueues work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hga {
+
+struct Dims {
+  int B, Hq, Hkv, D, Sq, Skv, top_k, top_g;
+  int q0;      // Skv - Sq: absolute position of the first query
+  int nblk;    // Sq / 64
+  float scale; // softmax scale
+  bool bf16;
+};
+
+hipError_t launch_summaries(const Dims& d, const void* K, float* chunk_mean, float* group_mean,
+                            int chunk_begin, int chunk_end, hipStream_t s);
+
+hipError_t launch_route(const Dims& d, const void* Q, const float* chunk_mean,
+                        const float* group_mean, int32_t* chunk_idx, int32_t* group_idx,
+                        hipStream_t s);
+
+hipError_t launch_attend_fwd(const Dims& d, const void* Q, const void* K, const void* V,
+                             const int32_t* group_idx, void* O, float* lse, hipStream_t s);
+
+hipError_t launch_attend_bwd_dq(const Dims& d, const void* Q, const void* K, const void* V,
+                                const void* O, const float* lse, const void* dO,
+                                const int32_t* group_idx, void* dQ, float* delta,
+                                hipStream_t s);
+
+hipError_t launch_attend_bwd_dkdv(const Dims& d, const void* Q, const void* K, const void* V,
+                                  const float* lse, const void* dO, const int32_t* group_idx,
+                                  const float* delta, void* dK, void* dV, hipStream_t s);
+
+}  // namespace hga

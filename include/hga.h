@@ -1,0 +1,176 @@
+/*
+ * hga.h -- C ABI of the MI355X (gfx950) Hierarchical Global Attention library.
+ *
+ * Source of the method: the page "BMW's 16 GB GPU just did what needs an
+ * A100" (seventnews.com, English edition), section "What HGA does
+ * differently".  HGA replaces the attention module; for every block of queries
+ * it routes over compact per-chunk summaries of the keys (64-token chunks),
+ * keeps the best chunks, opens them at the level of 8-token groups, keeps the
+ * best groups, and attends only the exact key/value tokens of those groups.
+ * The router has no weights: it scores the existing projected keys, and the
+ * summaries only steer selection (they are never keys or values).
+ *
+ * Readings fixed by this library where the page is silent:
+ *   - chunk summary = mean of the chunk's 64 keys; group summary = mean of the
+ *     group's 8 keys (both fp32);
+ *   - a query block is 64 consecutive queries; its routing query is the mean of
+ *     those 64 query vectors, and a score is the plain dot product (fp32);
+ *   - routing is per query head; query head h reads kv head h / (Hq / Hkv);
+ *   - the candidates of a block are the chunks strictly before the block's own
+ *     chunk; the own chunk is always attended, causally;
+ *   - top_g is chosen jointly over all 8 * kept-chunk groups;
+ *   - ranking is (score descending, index ascending); -0.0 ranks equal to +0.0;
+ *   - kept indices are written in ascending order, padded with -1;
+ *   - softmax scale 1/sqrt(head_dim) unless given; lse in natural log;
+ *   - the backward holds routing fixed (no gradient through the selection).
+ *
+ * Conventions for every call:
+ *   - all tensor pointers are DEVICE pointers to contiguous row-major buffers
+ *     owned by the caller, 16-byte aligned; outputs must not alias inputs;
+ *   - Q, O, dO, dQ are [B][Hq][q_len][D]; K, V, dK, dV are [B][Hkv][kv_len][D];
+ *     the q_len queries are the LAST q_len positions of the kv_len-long
+ *     sequence (a segment at the end of its history; q_len == kv_len is plain
+ *     causal self-attention);
+ *   - element type of Q, K, V, O, dO, dQ, dK, dV is shape->dtype (bf16 or fp32);
+ *     summaries, lse and the workspace are fp32; indices are int32;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); every
+ *     call only enqueues work on it: no allocation, no synchronisation, no
+ *     host<->device copy, no pointer kept after return;
+ *   - argument errors are reported before anything is launched and leave every
+ *     output untouched; a failed launch returns HGA_ERR_HIP; faults inside a
+ *     kernel surface at the caller's next synchronisation;
+ *   - calls are re-entrant: the library holds no mutable global state.
+ */
+#ifndef HGA_H_
+#define HGA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HGA_ABI_VERSION 1
+#define HGA_CHUNK 64      /* tokens per chunk (the page's 64-token chunks) */
+#define HGA_GROUP 8       /* tokens per group (the page's 8-token groups)  */
+#define HGA_QBLOCK 64     /* queries per routing block                      */
+#define HGA_MAX_TOP_K 64
+#define HGA_MAX_TOP_G 512
+#define HGA_MAX_KV_LEN 131072
+
+typedef enum {
+  HGA_OK = 0,
+  HGA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  HGA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes              */
+  HGA_ERR_UNSUPPORTED = 3, /* valid but unsupported (head_dim, dtype)         */
+  HGA_ERR_WORKSPACE = 4,   /* workspace missing or too small                  */
+  HGA_ERR_HIP = 5          /* a HIP launch failed                             */
+} hga_status;
+
+typedef enum { HGA_DTYPE_BF16 = 0, HGA_DTYPE_FP32 = 1 } hga_dtype;
+
+typedef struct {
+  int32_t batch;        /* B  >= 1                                            */
+  int32_t n_q_heads;    /* Hq >= 1, a multiple of n_kv_heads                  */
+  int32_t n_kv_heads;   /* Hkv >= 1                                           */
+  int32_t head_dim;     /* D in {64, 128}                                     */
+  int32_t q_len;        /* multiple of 64, 64 <= q_len <= kv_len              */
+  int32_t kv_len;       /* multiple of 64, <= HGA_MAX_KV_LEN                  */
+  int32_t top_k;        /* chunks kept per block, 0..HGA_MAX_TOP_K            */
+  int32_t top_g;        /* groups kept per block, 0..HGA_MAX_TOP_G            */
+  float softmax_scale;  /* <= 0 selects 1/sqrt(head_dim)                      */
+  int32_t dtype;        /* hga_dtype                                          */
+} hga_shape;
+
+/* ABI version (HGA_ABI_VERSION of the built library). */
+int hga_abi_version(void);
+
+/* Static text for a status code. */
+const char* hga_status_str(hga_status s);
+
+/* Host-only check of a shape against the limits above; touches no device. */
+hga_status hga_validate_shape(const hga_shape* shape);
+
+/* Chunk and group summaries of K (page section "What HGA does differently":
+ * one compact summary vector per 64-token chunk stays resident in GPU memory;
+ * the 8-token group summaries serve the second routing level).
+ *   K          [B][Hkv][kv_len][D]           dtype
+ *   chunk_mean [B][Hkv][kv_len/64][D]        fp32, written for chunks in
+ *                                            [chunk_begin, chunk_end) only
+ *   group_mean [B][Hkv][kv_len/8][D]         fp32, written for the groups of
+ *                                            those chunks only
+ * 0 <= chunk_begin <= chunk_end <= kv_len/64.  The range lets a caller append
+ * the summaries of new chunks to a resident history without rebuilding it. */
+hga_status hga_build_summaries(const hga_shape* shape, const void* K, float* chunk_mean,
+                               float* group_mean, int32_t chunk_begin, int32_t chunk_end,
+                               void* stream);
+
+/* Two-level routing (page section "What HGA does differently": score the
+ * chunk summaries, keep the top-k chunks, open them at group level, keep the
+ * best groups).  One routing row per (b, hq, block of 64 queries).
+ *   Q          [B][Hq][q_len][D]                       dtype
+ *   chunk_mean, group_mean                             as built above (all
+ *                                                      chunks before the last
+ *                                                      query block's own chunk
+ *                                                      must be built)
+ *   chunk_idx  [B][Hq][q_len/64][top_k]  int32, nullable when top_k == 0 or
+ *                                        the caller does not want it
+ *   group_idx  [B][Hq][q_len/64][top_g]  int32, nullable only when top_g == 0
+ * Row (b, hq, blk) keeps min(top_k, c) chunks among the c = (kv_len-q_len)/64
+ * + blk chunks before its own, then min(top_g, 8 * kept) groups of those
+ * chunks; both lists ascending, -1 padded. */
+hga_status hga_route(const hga_shape* shape, const void* Q, const float* chunk_mean,
+                     const float* group_mean, int32_t* chunk_idx, int32_t* group_idx,
+                     void* stream);
+
+/* Exact-token attention forward (page section "What HGA does differently":
+ * attention runs on the exact tokens of the kept groups).  The query at
+ * absolute position p of block blk attends every token of the row's kept
+ * groups plus its own chunk's tokens up to and including p.
+ *   group_idx  [B][Hq][q_len/64][top_g]  int32, as produced by hga_route
+ *              (ascending, -1 padded, every group before the own chunk)
+ *   O          [B][Hq][q_len][D]         dtype
+ *   lse        [B][Hq][q_len]            fp32 natural-log log-sum-exp of the
+ *                                        scaled logits, nullable */
+hga_status hga_attend_fwd(const hga_shape* shape, const void* Q, const void* K, const void* V,
+                          const int32_t* group_idx, void* O, float* lse, void* stream);
+
+/* Workspace bytes needed by the backward calls (fp32 row statistics). */
+hga_status hga_attend_bwd_workspace(const hga_shape* shape, size_t* bytes);
+
+/* Backward through the exact-token attention with the routing held fixed
+ * (page section "What HGA does differently": the router has no weights and
+ * gradients reach the same Q/K/V projections as dense attention).
+ *   O, lse     outputs of hga_attend_fwd for the same inputs
+ *   dO         [B][Hq][q_len][D]   dtype
+ *   dQ         [B][Hq][q_len][D]   dtype
+ *   dK, dV     [B][Hkv][kv_len][D] dtype; every position is written (zero
+ *              where no query attends); the sum over the Hq/Hkv query heads
+ *              of a kv head is formed in a fixed order, so results are
+ *              bitwise reproducible
+ *   workspace  device buffer of at least hga_attend_bwd_workspace() bytes */
+hga_status hga_attend_bwd(const hga_shape* shape, const void* Q, const void* K, const void* V,
+                          const void* O, const float* lse, const void* dO,
+                          const int32_t* group_idx, void* dQ, void* dK, void* dV,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two halves of hga_attend_bwd, for callers that schedule them apart.
+ * hga_attend_bwd_dq computes the row statistics delta = rowsum(dO * O) into
+ * the workspace and dQ; hga_attend_bwd_dkdv then reads delta from the same
+ * workspace and computes dK and dV.  The dkdv call must follow a dq call with
+ * the same inputs, on the same stream (or after it has completed). */
+hga_status hga_attend_bwd_dq(const hga_shape* shape, const void* Q, const void* K,
+                             const void* V, const void* O, const float* lse, const void* dO,
+                             const int32_t* group_idx, void* dQ, void* workspace,
+                             size_t workspace_bytes, void* stream);
+hga_status hga_attend_bwd_dkdv(const hga_shape* shape, const void* Q, const void* K,
+                               const void* V, const float* lse, const void* dO,
+                               const int32_t* group_idx, void* dK, void* dV,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HGA_H_ */

@@ -1,0 +1,80 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI on
+seeded inputs, and compare against the CPU oracle.  Nothing here feeds a GPU
+result into the oracle except routing indices for the attention comparison
+(so that near-tie routing differences cannot leak into output comparisons)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import hierarchical_routed_sparse_amd as hga
+from hierarchical_routed_sparse_amd import synthetic as syn
+from hga_testlib import allclose_report, tie_band_ok
+
+TOL = {"bf16": (2e-2, 1e-2), "fp32": (1e-5, 1e-5)}
+DEV = "cuda:0"
+
+
+def shape_of(w: syn.Workload, **kw):
+    base = dict(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                head_dim=w.head_dim, q_len=w.q_len, kv_len=w.kv_len, top_k=w.top_k,
+                top_g=w.top_g, dtype=w.dtype)
+    base.update(kw)
+    return hga.make_shape(**base)
+
+
+def upload(x: dict, dtype: str) -> dict:
+    return {k: syn.to_torch(v, dtype, DEV) for k, v in x.items()}
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def run_forward(w: syn.Workload, x: dict | None = None):
+    if x is None:
+        x = syn.make_inputs(w)
+    t = upload(x, w.dtype)
+    s = shape_of(w)
+    out = hga.forward(s, t["Q"], t["K"], t["V"])
+    torch.cuda.synchronize()
+    return s, x, t, out
+
+
+def check_routing(oracle, w, Qf, cm_o, gm_o, ci_gpu, gi_gpu, rows=None):
+    """GPU routing vs the oracle under the near-tie rule.  Returns the number of
+    rows where a near tie allowed a difference."""
+    ci_o, gi_o, cs, gs = oracle.route(Qf, cm_o, gm_o, w.kv_len, w.top_k, w.top_g,
+                                      want_scores=True)
+    tolerated = 0
+    forced = None
+    B, Hq, nblk = ci_gpu.shape[:3]
+    for idx in (rows if rows is not None else np.ndindex(B, Hq, nblk)):
+        a, b = ci_gpu[idx], ci_o[idx]
+        # format: ascending valid prefix, -1 padding
+        v = a[a >= 0]
+        assert np.all(np.diff(v) > 0) and np.all(a[len(v):] == -1), (idx, a)
+        if not np.array_equal(a, b):
+            ok, exact = tie_band_ok(a, b, cs[idx], w.top_k)
+            assert ok, f"chunk routing differs beyond the tie band at {idx}: {a} vs {b}"
+            tolerated += 1
+    # groups: against the oracle's choice given the GPU's chunk sets
+    if not np.array_equal(ci_gpu, ci_o):
+        _, gi_o, _, gs = oracle.route(Qf, cm_o, gm_o, w.kv_len, w.top_k, w.top_g,
+                                      forced_chunk_idx=ci_gpu, want_scores=True)
+    for idx in (rows if rows is not None else np.ndindex(B, Hq, nblk)):
+        a, b = gi_gpu[idx], gi_o[idx]
+        v = a[a >= 0]
+        assert np.all(np.diff(v) > 0) and np.all(a[len(v):] == -1), (idx, a)
+        if not np.array_equal(a, b):
+            ok, exact = tie_band_ok(a, b, gs[idx], w.top_g)
+            assert ok, f"group routing differs beyond the tie band at {idx}: {a} vs {b}"
+            tolerated += 1
+    return tolerated
+
+
+def assert_close(got, ref, dtype, what):
+    atol, rtol = TOL[dtype]
+    ok, maxerr, nbad = allclose_report(got, ref, atol, rtol)
+    assert ok, f"{what}: {nbad} elements beyond atol={atol} rtol={rtol}; max abs err {maxerr:.3e}"
+    return maxerr

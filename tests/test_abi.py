@@ -1,0 +1,100 @@
+"""The C-ABI library loads without a GPU, exports every declared entry point,
+and rejects bad arguments before launching anything (host-only checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hierarchical_routed_sparse_amd as hga
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "hga.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hga_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hga.lib_path()):
+        from hierarchical_routed_sparse_amd import build_lib
+        build_lib.build()
+    return ctypes.CDLL(hga.lib_path())
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"hga_build_summaries", "hga_route", "hga_attend_fwd", "hga_attend_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert hga.hga_abi_version() == 1
+
+
+def _ok_shape(**kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, q_len=2048, kv_len=16384,
+                top_k=16, top_g=64, dtype="bf16")
+    base.update(kw)
+    return hga.make_shape(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    ({"dtype": "fp32", "head_dim": 64}, 0),
+    ({"q_len": 16384}, 0),
+    ({"top_k": 0, "top_g": 0}, 0),
+    ({"batch": 0}, 2),
+    ({"n_q_heads": 30}, 2),              # not a multiple of n_kv_heads
+    ({"q_len": 100}, 2),                 # not a multiple of 64
+    ({"q_len": 0}, 2),
+    ({"kv_len": 1024}, 2),               # shorter than q_len
+    ({"kv_len": 16400}, 2),              # not a multiple of 64
+    ({"kv_len": 262144, "q_len": 2048}, 2),
+    ({"top_k": 65}, 2),
+    ({"top_k": -1}, 2),
+    ({"top_g": 513}, 2),
+    ({"head_dim": 96}, 3),
+    ({"dtype": 7}, 3),
+    ({"softmax_scale": float("nan")}, 2),
+])
+def test_validate_shape(kw, status):
+    assert hga.hga_validate_shape(_ok_shape(**kw)) == status
+
+
+def test_null_and_workspace_errors_before_launch(lib):
+    s = _ok_shape()
+    SP = ctypes.POINTER(hga.HgaShape)
+    lib.hga_build_summaries.argtypes = [SP] + [ctypes.c_void_p] * 3 + [ctypes.c_int32] * 2 + [ctypes.c_void_p]
+    assert lib.hga_build_summaries(ctypes.byref(s), None, None, None, 0, 256, None) == 1
+    # a non-null but bogus pointer with a bad chunk range is still rejected before launch
+    assert lib.hga_build_summaries(ctypes.byref(s), 16, 16, 16, 0, 257, None) == 2
+    assert lib.hga_build_summaries(ctypes.byref(s), 16, 16, 16, 5, 4, None) == 2
+    lib.hga_route.argtypes = [SP] + [ctypes.c_void_p] * 6
+    assert lib.hga_route(ctypes.byref(s), 16, 16, None, None, None, None) == 1   # top_g>0 needs group_idx
+    lib.hga_attend_fwd.argtypes = [SP] + [ctypes.c_void_p] * 7
+    assert lib.hga_attend_fwd(ctypes.byref(s), 16, 16, 16, None, 16, None, None) == 1
+    lib.hga_attend_bwd.argtypes = [SP] + [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p]
+    need = hga.hga_attend_bwd_workspace(s)
+    assert need >= 4 * 32 * 2048
+    args = [16] * 11
+    assert lib.hga_attend_bwd(ctypes.byref(s), *args[:10], None, need, None) == 4
+    assert lib.hga_attend_bwd(ctypes.byref(s), *args, need - 1, None) == 4
+    assert lib.hga_validate_shape(None) == 1
+
+
+def test_status_strings(lib):
+    lib.hga_status_str.restype = ctypes.c_char_p
+    for code in range(6):
+        assert lib.hga_status_str(code)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(hga, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(hga, "_lib", None)
+    with pytest.raises(hga.HGAError):
+        hga.hga_abi_version()
