@@ -1,0 +1,261 @@
+"""HGA forward + backward throughput on one MI355X.
+
+One step = the whole hot path over one batch of the 16K-context workload: chunk
+and group summaries of K, two-level routing, exact-token attention forward, and
+the backward (dQ, then dK/dV).  Workload: a 2048-query segment at the end of a
+16384-token history, 32 query / 8 kv heads, head_dim 128, chunk 64, group 8,
+top-k 16 chunks, top-g 64 groups, bf16, seeded synthetic inputs.  Inputs are
+resident in HBM before the timed region.
+
+Prints one JSON line: throughput in query tokens/s, per-phase kernel times from
+HIP events on the stream the kernels run on, the roofline of the dominant
+kernel, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HGA fwd+bwd query tokens/sec at 16K ctx, 1 MI355X; % HBM / % MFMA peak"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {
+    "summaries": ["summaries.hip"],
+    "route": ["route.hip"],
+    "attend_fwd": ["attend_fwd.hip"],
+    "attend_bwd_dq": ["attend_bwd.hip"],
+    "attend_bwd_dkdv": ["attend_bwd.hip"],
+}
+
+
+def source_hash(phase: str) -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "hierarchical_routed_sparse_amd", "csrc")
+    for f in KERNEL_SOURCES[phase] + ["hga_device.h"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="segment_2k_over_16k")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg (profiling runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 256 MiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_work(w, pairs: int) -> dict:
+    """Per-launch algorithmic bytes or flops of each phase (one launch per step)."""
+    B, Hq, Hkv, D, Sq, Skv = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.q_len, w.kv_len
+    esz = 2
+    means = B * Hkv * (Skv // 64 + Skv // 8) * D * 4
+    idx = B * Hq * (Sq // 64) * (w.top_k + w.top_g) * 4
+    return {
+        # read K once, write the fp32 chunk and group means once
+        "summaries": ("hbm", B * Hkv * Skv * D * esz + means),
+        # read Q once and the means once, write the indices
+        "route": ("hbm", B * Hq * Sq * D * esz + means + idx),
+        # 2 products (Q.K^T, P.V) of 2*D flops per attended pair
+        "attend_fwd": ("mfma", 4 * D * pairs),
+        # Q.K^T, dO.V^T, dS.K
+        "attend_bwd_dq": ("mfma", 6 * D * pairs),
+        # Q.K^T, dO.V^T, P^T.dO, dS^T.Q
+        "attend_bwd_dkdv": ("mfma", 8 * D * pairs),
+    }
+
+
+def attended_pairs(group_idx) -> int:
+    """Attended (query, key) pairs: 64*8 per kept group plus 64*65/2 causal
+    pairs of the own chunk, for every routing row."""
+    kept = int((group_idx >= 0).sum().item())
+    rows = group_idx.shape[0] * group_idx.shape[1] * group_idx.shape[2]
+    return 64 * 8 * kept + rows * (64 * 65 // 2)
+
+
+def load_traffic(phase: str):
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = rec.get("kernels", {}).get(phase)
+    if not r or r.get("source_sha") != source_hash(phase):
+        return None
+    return r.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x):
+    """The CPU oracle on one kv head and its query heads (1/Hkv of the layer):
+    summaries, routing, attention forward and backward, single thread."""
+    import oracle
+    from hierarchical_routed_sparse_amd import synthetic as syn
+    r = w.n_q_heads // w.n_kv_heads
+    xs = {"Q": x["Q"][:1, :r], "K": x["K"][:1, :1], "V": x["V"][:1, :1], "dO": x["dO"][:1, :r]}
+    xf = {k: syn.to_f64(v, w.dtype) for k, v in xs.items()}
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    cm, gm = oracle.summaries(xf["K"])
+    _, gi = oracle.route(xf["Q"], cm, gm, w.kv_len, w.top_k, w.top_g)
+    oracle.attend_fwd(xf["Q"], xf["K"], xf["V"], gi)
+    oracle.attend_bwd(xf["Q"], xf["K"], xf["V"], gi, xf["dO"])
+    dt = time.perf_counter() - t0
+    frac = w.batch * w.n_kv_heads   # the sample is one of B*Hkv equal kv groups
+    return {
+        "value": w.q_len * w.batch / (dt * frac),
+        "unit": "query tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"one kv head with its {r} query heads (1/{frac} of the layer) of the same "
+                   f"inputs: summaries, routing, attention forward and backward in fp64, "
+                   f"{dt:.2f} s single-threaded, scaled x{frac} to the whole layer"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the layer shards by kv head with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hierarchical_routed_sparse_amd as hga
+    from hierarchical_routed_sparse_amd import synthetic as syn
+
+    w = syn.WORKLOADS[args.workload]
+    x = syn.make_inputs(w, with_grad_output=True)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t = {k: syn.to_torch(v, w.dtype, dev) for k, v in x.items()}
+    s = hga.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.q_len, w.kv_len,
+                       w.top_k, w.top_g, dtype=w.dtype)
+    sz = hga._sizes(s)
+    f32, i32 = torch.float32, torch.int32
+    edt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    cm = torch.empty(sz["cm"], dtype=f32, device=dev)
+    gm = torch.empty(sz["gm"], dtype=f32, device=dev)
+    ci = torch.empty(sz["ci"], dtype=i32, device=dev)
+    gi = torch.empty(sz["gi"], dtype=i32, device=dev)
+    O = torch.empty(sz["q"], dtype=edt, device=dev)
+    lse = torch.empty(sz["lse"], dtype=f32, device=dev)
+    dQ = torch.empty(sz["q"], dtype=edt, device=dev)
+    dK = torch.empty(sz["kv"], dtype=edt, device=dev)
+    dV = torch.empty(sz["kv"], dtype=edt, device=dev)
+    ws = torch.empty(hga.hga_attend_bwd_workspace(s), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    phases = ["summaries", "route", "attend_fwd", "attend_bwd_dq", "attend_bwd_dkdv"]
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        hga.hga_build_summaries(s, t["K"], cm, gm, stream=stream)
+        if ev: ev[1].record(stream)
+        hga.hga_route(s, t["Q"], cm, gm, ci, gi, stream=stream)
+        if ev: ev[2].record(stream)
+        hga.hga_attend_fwd(s, t["Q"], t["K"], t["V"], gi, O, lse, stream=stream)
+        if ev: ev[3].record(stream)
+        hga.hga_attend_bwd_dq(s, t["Q"], t["K"], t["V"], O, lse, t["dO"], gi, dQ, ws,
+                              stream=stream)
+        if ev: ev[4].record(stream)
+        hga.hga_attend_bwd_dkdv(s, t["Q"], t["K"], t["V"], lse, t["dO"], gi, dK, dV, ws,
+                                stream=stream)
+        if ev: ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if args.calibrate_copy:
+        src = torch.ones(64 * 1024 * 1024, dtype=f32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / args.steps
+    phase_ms = {p: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+                for i, p in enumerate(phases)}
+    pairs = attended_pairs(gi)
+    work = algorithmic_work(w, pairs)
+    phase_rep = {}
+    for p in phases:
+        kind, amount = work[p]
+        sec = phase_ms[p] * 1e-3
+        if kind == "hbm":
+            ach = amount / sec / 1e9
+            phase_rep[p] = {"us": round(phase_ms[p] * 1e3, 2), "bound": "hbm",
+                            "achieved_GBs": round(ach, 1), "frac": round(ach / PEAK_HBM_GBS, 4)}
+        else:
+            ach = amount / sec / 1e12
+            phase_rep[p] = {"us": round(phase_ms[p] * 1e3, 2), "bound": "mfma",
+                            "achieved_TFLOPs": round(ach, 1),
+                            "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    dom = max(phases, key=lambda p: phase_ms[p])
+    kind, amount = work[dom]
+    sec = phase_ms[dom] * 1e-3
+    if kind == "hbm":
+        roof = {"bound": "hbm", "achieved": amount / sec / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": amount / sec / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = load_traffic(dom)
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = amount
+
+    base = None
+    if not args.no_cpu_baseline:
+        base = cpu_baseline(w, x)
+
+    out = {
+        "metric": METRIC,
+        "value": w.batch * w.q_len / (ms_step * 1e-3),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded clustered keys, N(0,1)/sqrt(128) queries and values)",
+        "config": {
+            "workload": f"{w.name} fwd+bwd",
+            "batch": w.batch, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
+            "head_dim": w.head_dim, "q_len": w.q_len, "kv_len": w.kv_len,
+            "chunk": 64, "group": 8, "top_k": w.top_k, "top_g": w.top_g,
+            "attended_pairs": pairs,
+        },
+        "roofline": roof,
+        "phases": phase_rep,
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -23,14 +23,18 @@ HEADERS = ["hga_device.h", "hga_kernels.h"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-fno-gpu-rdc", "-ffp-contract=fast",
+    # inputs are finite by contract: no NaN canonicalisation around min/max
+    "-mno-amdgpu-ieee", "-fno-honor-nans",
+    # MFMA accumulators in VGPRs (no AGPR round trips to rescale or read them)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     # packed fp32 instructions stay off: hipcc emits no v_pk_*_f32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra, build_dir=BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -38,20 +42,21 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compiles every HIP source and links libhga.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compiles every HIP source and links libhga.so (or `out`); returns its path.
+    `extra` holds additional hipcc flags, e.g. -D overrides of tuning constants."""
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, list(extra), build_dir), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

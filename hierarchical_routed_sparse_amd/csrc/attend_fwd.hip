@@ -7,20 +7,28 @@
 // of the block's kept groups and its own chunk up to p (causal).
 //
 // One workgroup (4 wavefronts) per (b, hq, block of 64 queries); wavefront w
-// owns queries 16w..16w+15.  The key/value set is processed in 64-token tiles:
+// owns queries 16w..16w+15.  The key/value set is walked in 64-token tiles:
 // tile 0 is the own chunk (causal mask), tile i >= 1 holds kept groups
-// 8(i-1)..8(i-1)+7 (each group is 8 contiguous rows, a 2 KB run of K and of V
-// at head_dim 128 in bf16).  Tiles are gathered from HBM into registers one
-// tile ahead and written to LDS: K row-major (16-byte units XOR-swizzled by
-// row), V transposed (so that the P.V product reads 4 consecutive keys per
-// 8-byte LDS read).  Per tile and wavefront:
-//   S^T[64 keys x 16 queries] = K . Q^T        (bf16 MFMA 16x16x32, fp32 acc)
+// 8(i-1)..8(i-1)+7 (a group is 8 contiguous rows: a 2 KB run of K and of V at
+// head_dim 128 in bf16).  Tiles are gathered straight from global memory into
+// LDS with 16-byte direct loads (no register staging), kStages tiles in
+// flight, row-major with 16-byte units XOR-swizzled by row.  Per tile and
+// wavefront:
+//   S^T[64 keys x 16 queries] = K . Q^T      bf16 MFMA 16x16x32, fp32 acc
 //   online softmax in the log2 domain (running max and sum per query)
-//   O^T[D x 16 queries]      += V^T . P^T      (bf16 MFMA, P rounded to bf16)
+//   O^T[D x 16 queries]      += V^T . P^T    bf16 MFMA; V^T read with the LDS
+//                                            transpose read, P kept in registers
 // The S^T accumulator layout (lane: one query, four keys) is directly the
-// operand layout of P^T for the second product, so P never leaves registers.
+// operand layout of P^T for the second product.
 #include "hga_device.h"
 #include "hga_kernels.h"
+
+#ifndef HGA_FWD_TILE
+#define HGA_FWD_TILE 32     // keys per tile: 32 (4 groups) or 64 (8 groups)
+#endif
+#ifndef HGA_FWD_STAGES
+#define HGA_FWD_STAGES 2    // tiles resident in LDS (STAGES - 1 in flight)
+#endif
 
 namespace hga {
 namespace {
@@ -38,23 +46,29 @@ struct FwdP {
   float scale;
 };
 
-template <typename T, int D> struct FwdCfg {
-  using RT = RowTile<T, D>;
-  using CT = ColTile<T, D>;
-  static constexpr int kStage = RT::kBytes + CT::kBytes;
-  static constexpr int kStages = 2 * kStage <= 140 * 1024 ? 2 : 1;
-  static constexpr int kPairs = 16 * (D / 8);   // pairs per 64-row matrix
-  static constexpr int kJobs = 2 * kPairs;      // K pairs, then V pairs
-  static constexpr int kJobsPerThread = (kJobs + kThreads - 1) / kThreads;
-};
+// The running max of a query is raised only when a tile's max exceeds it by
+// more than this many powers of two; until then P = 2^(x - m) <= 2^8, exact in
+// bf16 up to its usual relative rounding, and the O accumulators need no
+// rescaling on most tiles.
+constexpr float kRescale = 8.0f;
 
-template <typename T, int D>
+template <typename T, int D, int TK, int S>
 __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
-  using Cfg = FwdCfg<T, D>;
-  using RT = typename Cfg::RT;
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::kStages * Cfg::kStage];
+  using RT = RowTile<T, D>;
+  constexpr int kTileBytes = TK * RT::kUnits * 16;                 // one matrix, TK rows
+  constexpr int kStage = 2 * kTileBytes;                          // K tile | V tile
+  constexpr int kRowsPerWave = TK / 4;
+  constexpr int kRPI = rows_per_issue<T, D>();
+  constexpr int kIssues = kRowsPerWave / kRPI;                    // per matrix per wave
+  constexpr int kLoads = 2 * kIssues;                             // per wave per tile
+  constexpr int kLocalTiles = kChunk / TK;
+  constexpr int kGroupsPerTile = TK / kGroup;
+  constexpr int NKS = TK / 16;   // 16-key subtiles
+  constexpr int NMM = TK / 32;   // 32-key slices of the P.V product
+  static_assert(kRowsPerWave % kRPI == 0, "tile rows per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[S * kStage];
   __shared__ int s_glist[kMaxTopG];
-  __shared__ int s_glast;
+  __shared__ int s_wsum[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -69,17 +83,26 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
   const int cb = p.q0 / kChunk + blk;
   const long long row = ((long long)b * p.Hq + hq) * p.nblk + blk;
 
-  // routing row -> LDS; entries outside [0, 8*cb) are ignored
-  if (tid == 0) s_glast = 0;
-  __syncthreads();
-  for (int i = tid; i < p.top_g; i += kThreads) {
-    const int gm = p.gidx[row * p.top_g + i];
+  // routing row -> LDS, keeping only groups in [0, 8*cb), compacted in order
+  int nvalid = 0;
+  for (int i0 = 0; i0 < p.top_g; i0 += kThreads) {
+    const int i = i0 + tid;
+    const int gm = i < p.top_g ? p.gidx[row * p.top_g + i] : -1;
     const bool ok = gm >= 0 && gm < cb * 8;
-    s_glist[i] = ok ? gm : -1;
-    if (ok) atomicMax(&s_glast, i + 1);
+    const uint64_t bal = __ballot(ok);
+    if (lane == 0) s_wsum[wv] = __popcll(bal);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      off += k < wv ? s_wsum[k] : 0;
+      tot += s_wsum[k];
+    }
+    if (ok) s_glist[nvalid + off + mbcnt(bal)] = gm;
+    nvalid += tot;
+    __syncthreads();
   }
-  __syncthreads();
-  const int ntiles = 1 + (s_glast + 7) / 8;
+  const int ntiles = kLocalTiles + (nvalid + kGroupsPerTile - 1) / kGroupsPerTile;
 
   const T* Kbh = reinterpret_cast<const T*>(p.K) + (long long)bh * p.Skv * D;
   const T* Vbh = reinterpret_cast<const T*>(p.V) + (long long)bh * p.Skv * D;
@@ -93,43 +116,30 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
     for (int s = 0; s < D / 32; ++s) load_frag(qf[s], q + 32 * s);
   }
 
-  Pair<T> st[Cfg::kJobsPerThread];
-  auto load_tile = [&](int ti) {
+  // Tiles 0..kLocalTiles-1 cover the own chunk; later tiles hold
+  // kGroupsPerTile kept groups.  A slot past the last kept group reads the own
+  // chunk (any valid row works: its scores are masked, its P is exactly zero).
+  const uint32_t smem_lds = lds_addr(smem);
+  auto issue = [&](int ti) {
+    const uint32_t buf = smem_lds + (uint32_t)((ti % S) * kStage);
+    uint32_t off[kIssues];
 #pragma unroll
-    for (int u = 0; u < Cfg::kJobsPerThread; ++u) {
-      const int job = tid + kThreads * u;
-      if (job < Cfg::kJobs) {
-        const bool isv = job >= Cfg::kPairs;
-        const int pr = isv ? job - Cfg::kPairs : job;
-        const int q = pr / (D / 8), o = pr % (D / 8);
-        long long tok = -1;
-        if (ti == 0) {
-          tok = (long long)cb * kChunk + 4 * q;
-        } else {
-          const int slot = 8 * (ti - 1) + (q >> 1);
-          const int gm = slot < p.top_g ? s_glist[slot] : -1;
-          if (gm >= 0) tok = (long long)gm * kGroup + 4 * (q & 1);
-        }
-        if (tok >= 0)
-          load_pair(st[u], (isv ? Vbh : Kbh) + tok * D + 8 * o, D);
-        else
-          zero_pair(st[u]);
+    for (int j = 0; j < kIssues; ++j) {
+      const int rr = kRowsPerWave * wv + kRPI * j + lane / RT::kUnits;
+      uint32_t tok = (uint32_t)(cb * kChunk + (rr & (kChunk - 1)));
+      if (ti < kLocalTiles) {
+        tok += (uint32_t)(ti * TK);
+      } else {
+        const int slot = kGroupsPerTile * (ti - kLocalTiles) + (rr >> 3);
+        if (slot < nvalid) tok = (uint32_t)(s_glist[slot] * kGroup + (rr & 7));
       }
+      off[j] = dma_offset<T, D>(rr, tok);
     }
-  };
-  auto store_tile = [&](char* buf) {
 #pragma unroll
-    for (int u = 0; u < Cfg::kJobsPerThread; ++u) {
-      const int job = tid + kThreads * u;
-      if (job < Cfg::kJobs) {
-        const bool isv = job >= Cfg::kPairs;
-        const int pr = isv ? job - Cfg::kPairs : job;
-        const int q = pr / (D / 8), o = pr % (D / 8);
-        if (isv)
-          store_pair_cols<D>(buf + RT::kBytes, st[u], q, o);
-        else
-          store_pair_rows<D>(buf, st[u], q, o);
-      }
+    for (int j = 0; j < kIssues; ++j) {
+      const uint32_t dst = buf + (uint32_t)((kRowsPerWave * wv + kRPI * j) * RT::kUnits * 16);
+      dma16_off(off[j], Kbh, dst);
+      dma16_off(off[j], Vbh, dst + kTileBytes);
     }
   };
 
@@ -140,77 +150,113 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
   const float c2 = p.scale * kLog2e;
   const int qq = 16 * wv + l16;   // this lane's query within the block
 
-  load_tile(0);
-  store_tile(smem);
-  __syncthreads();
-  for (int ti = 0; ti < ntiles; ++ti) {
-    if (ti + 1 < ntiles) load_tile(ti + 1);
-    const char* buf = smem + (Cfg::kStages == 2 ? (ti & 1) : 0) * Cfg::kStage;
-
-    // S^T = K . Q^T for 4 subtiles of 16 keys
-    f32x4 sacc[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+  for (int ti = 0; ti < S - 1; ++ti)
+    if (ti < ntiles) issue(ti);
+
+  for (int ti = 0; ti < ntiles; ++ti) {
+    // tile ti has landed once at most (tiles issued after it) x kLoads remain
+    const int ahead = (ntiles - 1 - ti) < (S - 2) ? (ntiles - 1 - ti) : (S - 2);
+    if (ahead >= 3) wait_vmcnt<3 * kLoads>();
+    else if (ahead == 2) wait_vmcnt<2 * kLoads>();
+    else if (ahead == 1) wait_vmcnt<kLoads>();
+    else wait_vmcnt<0>();
+    __syncthreads();   // tile ti visible to all; everyone is done with tile ti-1
+    if (ti + S - 1 < ntiles) issue(ti + S - 1);
+
+    const char* kt = smem + (ti % S) * kStage;
+    const char* vt = kt + kTileBytes;
+
+    // S^T = K . Q^T for NKS subtiles of 16 keys (raw dot products)
+    f32x4 sacc[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
       sacc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
         Frag<T> kf;
-        frag_rows<T, D>(kf, buf, 16 * ks + l16, s, g4);
+        frag_rows<T, D>(kf, kt, 16 * ks + l16, s, g4);
         mma(sacc[ks], kf, qf[s]);
       }
     }
-    // mask, running max
-    float mt = -INFINITY;
+    // masks: causal on the own chunk, empty slots on the last group tile
+    if (ti < kLocalTiles) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bool gvalid = true;
-      if (ti > 0) {
-        const int slot = 8 * (ti - 1) + 2 * ks + (g4 >> 1);
-        gvalid = slot < p.top_g && s_glist[slot] >= 0;
-      }
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = 16 * ks + 4 * g4 + i;
-        const bool valid = ti == 0 ? kk <= qq : gvalid;
-        const float x = valid ? sacc[ks][i] * c2 : -INFINITY;
-        sacc[ks][i] = x;
-        mt = fmaxf(mt, x);
+        for (int i = 0; i < 4; ++i)
+          if (TK * ti + 16 * ks + 4 * g4 + i > qq) sacc[ks][i] = -INFINITY;
+    } else if (kGroupsPerTile * (ti - kLocalTiles + 1) > nvalid) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int slot = kGroupsPerTile * (ti - kLocalTiles) + 2 * ks + (g4 >> 1);
+        if (slot >= nvalid) sacc[ks] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       }
     }
-    mt = xor_max16_32(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      mx = fmaxf(fmaxf(mx, fmaxf(sacc[ks][0], sacc[ks][1])), fmaxf(sacc[ks][2], sacc[ks][3]));
+    const float mc = xor_max16_32(mx) * c2;
+    const bool raise = mc > m_run + kRescale;
+    if (__ballot(raise)) {
+      const float m_new = raise ? mc : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) oacc[i] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_amdgcn_exp2f(sacc[ks][i] - m_new);
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[ks][i], c2, -m_run));
         sacc[ks][i] = e;
         psum += e;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) oacc[i] *= alpha;
+    l_run += psum;
 
-    // O^T += V^T . P^T
-    Frag<T> pf[2];
-    frag_from_acc(pf[0], sacc[0], sacc[1]);
-    frag_from_acc(pf[1], sacc[2], sacc[3]);
-    const char* vt = buf + RT::kBytes;
+    // O^T += V^T . P^T ; P^T items of key slice mm: keys 32mm+4g+t, 32mm+16+4g+t
+    Frag<T> pf[NMM];
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds)
+    for (int mm = 0; mm < NMM; ++mm) frag_from_acc(pf[mm], sacc[2 * mm], sacc[2 * mm + 1]);
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t vbase = lds_addr(vt);
+      uint32_t rb[2 * NMM];   // (mm, half): rows 32mm + 16h + 4g + (l16 >> 2)
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        Frag<T> vf;
-        frag_cols<T, D>(vf, vt, 16 * ds + l16, mm, g4);
-        mma(oacc[ds], vf, pf[mm]);
+      for (int mm = 0; mm < NMM; ++mm)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) rb[2 * mm + h] = tr_base<D>(vbase, 32 * mm + 16 * h + 4 * g4 + (l16 >> 2));
+      constexpr int NF = (D / 16) * NMM;   // fragments, index f = ds * NMM + mm
+#pragma unroll
+      for (int f0 = 0; f0 < NF; f0 += 4) {
+        uint32_t a[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int f = f0 + i, ds = f / NMM, mm = f % NMM;
+          a[2 * i] = rb[2 * mm] ^ (uint32_t)(32 * ds);
+          a[2 * i + 1] = rb[2 * mm + 1] ^ (uint32_t)(32 * ds);
+        }
+        Frag<T> vf[4];
+        tr_frags4(vf, a);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int f = f0 + i, ds = f / NMM, mm = f % NMM;
+          mma(oacc[ds], vf[i], pf[mm]);
+        }
       }
-
-    if (Cfg::kStages == 1) __syncthreads();
-    if (ti + 1 < ntiles) store_tile(smem + (Cfg::kStages == 2 ? ((ti + 1) & 1) : 0) * Cfg::kStage);
-    __syncthreads();
+    } else {
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+        for (int mm = 0; mm < NMM; ++mm) {
+          Frag<T> vf;
+          frag_tr<T, D>(vf, vt, 32 * mm + 4 * g4, 32 * mm + 16 + 4 * g4, 16 * ds);
+          mma(oacc[ds], vf, pf[mm]);
+        }
+    }
   }
 
   // epilogue: normalise, write O (4 consecutive elements per lane) and lse
@@ -231,7 +277,13 @@ hipError_t run(const Dims& d, const void* Q, const void* K, const void* V, const
   p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.q0 = d.q0;
   p.nblk = d.nblk; p.top_g = d.top_g; p.scale = d.scale;
   p.nwork = d.B * d.Hq * d.nblk;
-  attend_fwd_kernel<T, D><<<p.nwork, kThreads, 0, s>>>(p);
+  // fp32 tiles are twice as large: cap the stages at 128 KB of LDS
+  constexpr int TK = HGA_FWD_TILE;
+  constexpr int kStageBytes = 2 * TK * D * (int)sizeof(T);
+  constexpr int S0 = HGA_FWD_STAGES;
+  constexpr int S = S0 * kStageBytes <= 128 * 1024 ? S0 : (128 * 1024) / kStageBytes;
+  static_assert(S >= 2, "at least two stages");
+  attend_fwd_kernel<T, D, TK, S><<<p.nwork, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -32,19 +32,21 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
-// fp32 -> bf16, round to nearest even (inputs here are finite).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// fp32 pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 template <typename T> struct Elem;
 template <> struct Elem<uint16_t> { static constexpr int kBytes = 2; };
 template <> struct Elem<float> { static constexpr int kBytes = 4; };
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
 
 // ----------------------------------------------------------------- wave helpers
 
@@ -55,15 +57,23 @@ __device__ __forceinline__ int mbcnt(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (the same column of a
+// 16x16 MFMA accumulator).  v_permlane32_swap exchanges the upper half of its
+// first operand with the lower half of its second; with both operands equal to
+// v, the two results hold v and its lane-xor-32 partner in some order, so
+// their max (sum) is the pairwise max (sum).  v_permlane16_swap does the same
+// for lane-xor-16 partners.
 __device__ __forceinline__ float xor_max16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float xor_sum16_32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Work index for block `bid` such that consecutive work indices land on the
@@ -274,6 +284,184 @@ __device__ __forceinline__ void frag_cols(Frag<T>& f, const char* tile, int e, i
   constexpr int S = ColTile<T, D>::kStride;
   const T* t = reinterpret_cast<const T*>(tile) + e * S + 32 * m + 4 * g;
   load_frag_split(f, t, t + 16);
+}
+
+
+// ----------------------------------------------------------------- async tile fill
+//
+// global_load_lds_dwordx4 (gfx950): every lane of a wavefront moves 16 bytes
+// from its own global address into LDS at M0 + 16 * lane, so one instruction
+// fills 1 KB of LDS.  A row-major swizzled tile is filled by choosing, for LDS
+// unit (row, physical unit p), the global source (row, logical unit
+// p ^ swz(row)).  Completion is tracked by vmcnt.
+//
+// The load is issued from inline asm: the compiler then never treats it as a
+// pending LDS write, so it does not put a full vmcnt wait in front of every
+// LDS read (which would serialise the tile pipeline).  The instruction has no
+// register result; the kernels wait with wait_vmcnt<N>() plus a barrier
+// before reading a tile.  M0 is saved and restored inside the block.
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] + vmcnt[5:4] at bits 15:14, expcnt 6:4, lgkmcnt 11:8
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+// Same load with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (no 64-bit address arithmetic per lane).
+__device__ __forceinline__ void dma16_off(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  // force the base into SGPRs (it is wave-uniform by construction)
+  // (readfirstlane returns int: widen through uint32_t so that the low half is
+  // zero-extended, never sign-extended)
+  const uint64_t b64 = (uint64_t)(uintptr_t)sbase;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b64);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b64 >> 32));
+  sbase = (const void*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+template <typename T, int D>
+__device__ constexpr int rows_per_issue() { return 64 / RowTile<T, D>::kUnits; }
+
+// Byte offset, relative to element 0 of token 0, of the 16-byte unit this
+// lane moves for tile row `row` when the row holds token `tok`.
+template <typename T, int D>
+__device__ __forceinline__ uint32_t dma_offset(int row, uint32_t tok) {
+  constexpr int U = RowTile<T, D>::kUnits;
+  const int phys = lane_id() % U;
+  return tok * (uint32_t)(D * Elem<T>::kBytes) + (uint32_t)((phys ^ RowTile<T, D>::swz(row)) << 4);
+}
+
+// Issues the loads of `nrows` rows starting at row r0 (nrows a multiple of
+// rows_per_issue()) of a row-major swizzled tile at LDS byte address `tile`;
+// rowptr(row) returns the global address of element 0 of that row.  Every
+// wavefront that calls this issues nrows / rows_per_issue() loads.
+template <typename T, int D, typename RowPtr>
+__device__ __forceinline__ void fill_rows_async(uint32_t tile, int r0, int nrows, RowPtr rowptr) {
+  constexpr int U = RowTile<T, D>::kUnits;
+  constexpr int RPI = 64 / U;
+  constexpr int EPU = 16 / Elem<T>::kBytes;   // elements per 16-byte unit
+  const int lane = lane_id();
+#pragma unroll
+  for (int j = 0; j < nrows; j += RPI) {
+    const int row = r0 + j + lane / U;
+    const int phys = lane % U;
+    const T* src = rowptr(row) + (phys ^ RowTile<T, D>::swz(row)) * EPU;
+    dma16(src, __builtin_amdgcn_readfirstlane(tile + (uint32_t)((r0 + j) * U * 16)));
+  }
+}
+
+// ----------------------------------------------------------------- transposed operand reads
+//
+// Operand fragment whose 8 items run down a column of a row-major swizzled
+// tile: items 0..3 = tile[ra + t][d0 + l16], items 4..7 = tile[rb + t][d0 + l16]
+// (ra, rb may differ per 16-lane group).  bf16 uses ds_read_b64_tr_b16: in a
+// 16-lane group, lane j points at the 4 elements tile[r + j/4][d0 + 4(j%4) ..],
+// and the hardware hands lane i the column tile[r + 0..3][d0 + i].
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+template <typename T, int D>
+__device__ __forceinline__ void frag_tr(Frag<T>& f, const char* tile, int ra, int rb, int d0) {
+  const int l16 = lane_id() & 15;
+  if constexpr (Elem<T>::kBytes == 2) {
+    const int col = d0 + 4 * (l16 & 3);
+    const int unit = col >> 3, half = (col >> 2) & 1;
+    const int r1 = ra + (l16 >> 2), r2 = rb + (l16 >> 2);
+    const char* a1 = tile + RowTile<T, D>::off(r1, unit) + 8 * half;
+    const char* a2 = tile + RowTile<T, D>::off(r2, unit) + 8 * half;
+    const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)a1);
+    const v4i16 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)a2);
+    f.w[0] = (uint32_t)(uint16_t)x[0] | ((uint32_t)(uint16_t)x[1] << 16);
+    f.w[1] = (uint32_t)(uint16_t)x[2] | ((uint32_t)(uint16_t)x[3] << 16);
+    f.w[2] = (uint32_t)(uint16_t)y[0] | ((uint32_t)(uint16_t)y[1] << 16);
+    f.w[3] = (uint32_t)(uint16_t)y[2] | ((uint32_t)(uint16_t)y[3] << 16);
+  } else {
+    const int col = d0 + l16;
+    const int unit = col >> 2, sub = col & 3;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f.v[t] = *reinterpret_cast<const float*>(tile + RowTile<T, D>::off(ra + t, unit) + 4 * sub);
+      f.v[4 + t] = *reinterpret_cast<const float*>(tile + RowTile<T, D>::off(rb + t, unit) + 4 * sub);
+    }
+  }
+}
+
+
+// ----------------------------------------------------------------- batched transpose reads
+//
+// The compiler cannot tell whether an LDS transpose read aliases an LDS
+// direct load still in flight and would wait for every outstanding global
+// load before the first one, which serialises the tile pipeline.  These
+// helpers issue eight ds_read_b64_tr_b16 and wait for them inside the same
+// asm block, so no outstanding result ever leaves the block.
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void tr_read8(u32x2 (&o)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
+// LDS byte address of the transpose-read row pointer for tile row `row`,
+// column block 0 (columns 0..15), of a bf16 row-major swizzled tile at `tile`.
+// The address for column block cb (columns 16cb..16cb+15) is base ^ (32 * cb):
+// lane j of a 16-lane group points at columns 4(j%4)..+3 of its row, i.e. unit
+// (j%4)/2, half j%2; with units XOR-swizzled by the row, stepping the column
+// block flips bit 5 of the byte offset only.
+template <int D>
+__device__ __forceinline__ uint32_t tr_base(uint32_t tile, int row) {
+  using RT = RowTile<uint16_t, D>;
+  const int j = lane_id() & 15;
+  const int u0 = (j & 3) >> 1, half = j & 1;
+  return tile + (uint32_t)(row * RT::kUnits * 16) + (uint32_t)(((u0 ^ RT::swz(row)) << 4) | (half << 3));
+}
+
+// Two operand fragments from 8 transpose reads: f[i] items 0..3 from a[2i],
+// items 4..7 from a[2i+1], for i = 0..3.
+__device__ __forceinline__ void tr_frags4(Frag<uint16_t> (&f)[4], const uint32_t (&a)[8]) {
+  u32x2 o[8];
+  tr_read8(o, a);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i].w[0] = o[2 * i][0]; f[i].w[1] = o[2 * i][1];
+    f[i].w[2] = o[2 * i + 1][0]; f[i].w[3] = o[2 * i + 1][1];
+  }
 }
 
 }  // namespace hga
