@@ -3,6 +3,7 @@
 #include "../../include/hga.h"
 
 #include <math.h>
+#include <string.h>
 
 #include "hga_kernels.h"
 
@@ -59,7 +60,11 @@ hga_status hga_validate_shape(const hga_shape* s) {
     return HGA_ERR_SHAPE;
   if (s->top_k < 0 || s->top_k > HGA_MAX_TOP_K) return HGA_ERR_SHAPE;
   if (s->top_g < 0 || s->top_g > HGA_MAX_TOP_G) return HGA_ERR_SHAPE;
-  if (!(s->softmax_scale == s->softmax_scale)) return HGA_ERR_SHAPE;   // NaN
+  // NaN or infinite scale (checked on the bit pattern: the library is built
+  // with -fno-honor-nans, under which x != x may be folded away)
+  uint32_t sbits;
+  memcpy(&sbits, &s->softmax_scale, sizeof(sbits));
+  if ((sbits & 0x7F800000u) == 0x7F800000u) return HGA_ERR_SHAPE;
   if (s->head_dim != 64 && s->head_dim != 128) return HGA_ERR_UNSUPPORTED;
   if (s->dtype != HGA_DTYPE_BF16 && s->dtype != HGA_DTYPE_FP32) return HGA_ERR_UNSUPPORTED;
   // launch sizes must fit a 32-bit grid

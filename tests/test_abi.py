@@ -61,6 +61,8 @@ def _ok_shape(**kw):
     ({"head_dim": 96}, 3),
     ({"dtype": 7}, 3),
     ({"softmax_scale": float("nan")}, 2),
+    ({"softmax_scale": float("inf")}, 2),
+    ({"softmax_scale": -1.0}, 0),                 # <= 0 selects 1/sqrt(head_dim)
 ])
 def test_validate_shape(kw, status):
     assert hga.hga_validate_shape(_ok_shape(**kw)) == status
