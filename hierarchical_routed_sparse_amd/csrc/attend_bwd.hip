@@ -10,23 +10,82 @@
 //   dQ      = scale * dS . K      dK = scale * dS^T . Q      dV = P^T . dO
 //
 // Two kernels:
-//  * bwd_dq  -- one workgroup per (b, hq, block), the same tile walk as the
-//    forward (own chunk, then 8 kept groups per tile); writes delta and dQ.
+//  * bwd_dq  -- one workgroup per (b, hq, block): the forward's tile walk (own
+//    chunk, then the kept groups), K and V tiles gathered into LDS with direct
+//    loads; writes delta and dQ.  dQ^T += K^T . dS^T reads K^T with the LDS
+//    transpose read.
 //  * bwd_dkdv -- one workgroup per (b, hkv, chunk of 64 keys).  It finds, for
 //    every (query head of the kv group, query block), which of the chunk's 8
 //    groups that row kept (binary search in the ascending routing row) or
 //    whether the chunk is the row's own chunk (causal), compacts those rows in
-//    a fixed order, and walks them: wavefront w owns keys 16w..16w+15 and skips
-//    rows that kept neither of its two groups.  Each key's dK/dV is summed by
-//    one wavefront in that fixed order: no atomics, bitwise reproducible.
+//    a fixed order, and walks them with the rows' Q and dO tiles gathered into
+//    LDS by direct loads; wavefront w owns keys 16w..16w+15 and skips rows that
+//    kept neither of its two groups.  Each key's dK/dV is summed by one
+//    wavefront in that fixed order: no atomics, bitwise reproducible.
 #include "hga_device.h"
 #include "hga_kernels.h"
+
+#ifndef HGA_DQ_TILE
+#define HGA_DQ_TILE 32
+#endif
+#ifndef HGA_DQ_STAGES
+#define HGA_DQ_STAGES 2
+#endif
+#ifndef HGA_DKV_STAGES
+#define HGA_DKV_STAGES 2
+#endif
 
 namespace hga {
 namespace {
 
 constexpr int kMaxTopG = 512;
 constexpr int kRowsPerPass = 1024;   // routing rows examined per entry-list build
+
+// Compacts the routing row (groups in [0, 8*cb), order kept) into s_glist and
+// returns how many were kept.  Every thread of the workgroup must call it.
+__device__ __forceinline__ int load_routing_row(const int32_t* grow, int top_g, int cb,
+                                                int* s_glist, int* s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int nvalid = 0;
+  for (int i0 = 0; i0 < top_g; i0 += kThreads) {
+    const int i = i0 + tid;
+    const int gm = i < top_g ? grow[i] : -1;
+    const bool ok = gm >= 0 && gm < cb * 8;
+    const uint64_t bal = __ballot(ok);
+    if (lane == 0) s_wsum[wv] = __popcll(bal);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      off += k < wv ? s_wsum[k] : 0;
+      tot += s_wsum[k];
+    }
+    if (ok) s_glist[nvalid + off + mbcnt(bal)] = gm;
+    nvalid += tot;
+    __syncthreads();
+  }
+  return nvalid;
+}
+
+// 8 operand fragments of a transposed read of tile rows: fragment f covers
+// column block cbk[f] and row bases rows (ra[f], rb[f]) as in frag_tr.
+template <typename T, int D>
+__device__ __forceinline__ void tr_frags(Frag<T> (&out)[4], const char* tile, const int (&ra)[4],
+                                         const int (&rb)[4], const int (&cbk)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t base = lds_addr(tile);
+    uint32_t a[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[2 * i] = tr_base<D>(base, ra[i]) ^ (uint32_t)(32 * cbk[i]);
+      a[2 * i + 1] = tr_base<D>(base, rb[i]) ^ (uint32_t)(32 * cbk[i]);
+    }
+    tr_frags4(out, a);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) frag_tr<T, D>(out[i], tile, ra[i], rb[i], 16 * cbk[i]);
+  }
+}
 
 // ============================================================== dQ
 
@@ -44,24 +103,23 @@ struct DqP {
   float scale;
 };
 
-template <typename T, int D> struct DqCfg {
-  using RT = RowTile<T, D>;
-  using CT = ColTile<T, D>;
-  // stage: K rows | V rows | K transposed
-  static constexpr int kStage = 2 * RT::kBytes + CT::kBytes;
-  static constexpr int kStages = 2 * kStage <= 140 * 1024 ? 2 : 1;
-  static constexpr int kPairs = 16 * (D / 8);
-  static constexpr int kJobs = 2 * kPairs;      // K pairs, then V pairs
-  static constexpr int kJobsPerThread = (kJobs + kThreads - 1) / kThreads;
-};
-
-template <typename T, int D>
+template <typename T, int D, int TK, int S>
 __global__ __launch_bounds__(kThreads) void attend_bwd_dq_kernel(const DqP p) {
-  using Cfg = DqCfg<T, D>;
-  using RT = typename Cfg::RT;
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::kStages * Cfg::kStage];
+  using RT = RowTile<T, D>;
+  constexpr int kTileBytes = TK * RT::kUnits * 16;
+  constexpr int kStage = 2 * kTileBytes;                          // K tile | V tile
+  constexpr int kRowsPerWave = TK / 4;
+  constexpr int kRPI = rows_per_issue<T, D>();
+  constexpr int kIssues = kRowsPerWave / kRPI;
+  constexpr int kLoads = 2 * kIssues;
+  constexpr int kLocalTiles = kChunk / TK;
+  constexpr int kGroupsPerTile = TK / kGroup;
+  constexpr int NKS = TK / 16;
+  constexpr int NMM = TK / 32;
+  static_assert(kRowsPerWave % kRPI == 0, "tile rows per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[S * kStage];
   __shared__ int s_glist[kMaxTopG];
-  __shared__ int s_glast;
+  __shared__ int s_wsum[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -75,23 +133,15 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dq_kernel(const DqP p) {
   const int cb = p.q0 / kChunk + blk;
   const long long row = ((long long)b * p.Hq + hq) * p.nblk + blk;
 
-  if (tid == 0) s_glast = 0;
-  __syncthreads();
-  for (int i = tid; i < p.top_g; i += kThreads) {
-    const int gm = p.gidx[row * p.top_g + i];
-    const bool ok = gm >= 0 && gm < cb * 8;
-    s_glist[i] = ok ? gm : -1;
-    if (ok) atomicMax(&s_glast, i + 1);
-  }
-  __syncthreads();
-  const int ntiles = 1 + (s_glast + 7) / 8;
+  const int nvalid = load_routing_row(p.gidx + row * p.top_g, p.top_g, cb, s_glist, s_wsum);
+  const int ntiles = kLocalTiles + (nvalid + kGroupsPerTile - 1) / kGroupsPerTile;
 
   const T* Kbh = reinterpret_cast<const T*>(p.K) + (long long)bh * p.Skv * D;
   const T* Vbh = reinterpret_cast<const T*>(p.V) + (long long)bh * p.Skv * D;
   const long long qrow0 = ((long long)b * p.Hq + hq) * p.Sq + (long long)blk * kChunk;
   const int qq = 16 * wv + l16;
 
-  // Q and dO of this wavefront's 16 queries (B operands); delta from dO . O
+  // Q and dO of this wavefront's 16 queries (B operands); delta = dO . O
   Frag<T> qf[D / 32], dof[D / 32];
   float delta;
   {
@@ -109,50 +159,31 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dq_kernel(const DqP p) {
       part += frag_dot(dof[s], of);
     }
     delta = xor_sum16_32(part);
-    if (g4 == 0) p.delta[qrow0 + qq] = delta;
   }
-  const float lse2 = p.lse[qrow0 + qq] * kLog2e;
+  const float nlse2 = -p.lse[qrow0 + qq] * kLog2e;
   const float c2 = p.scale * kLog2e;
 
-  Pair<T> st[Cfg::kJobsPerThread];
-  auto load_tile = [&](int ti) {
+  const uint32_t smem_lds = lds_addr(smem);
+  auto issue = [&](int ti) {
+    const uint32_t buf = smem_lds + (uint32_t)((ti % S) * kStage);
+    uint32_t off[kIssues];
 #pragma unroll
-    for (int u = 0; u < Cfg::kJobsPerThread; ++u) {
-      const int job = tid + kThreads * u;
-      if (job < Cfg::kJobs) {
-        const bool isv = job >= Cfg::kPairs;
-        const int pr = isv ? job - Cfg::kPairs : job;
-        const int q = pr / (D / 8), o = pr % (D / 8);
-        long long tok = -1;
-        if (ti == 0) {
-          tok = (long long)cb * kChunk + 4 * q;
-        } else {
-          const int slot = 8 * (ti - 1) + (q >> 1);
-          const int gm = slot < p.top_g ? s_glist[slot] : -1;
-          if (gm >= 0) tok = (long long)gm * kGroup + 4 * (q & 1);
-        }
-        if (tok >= 0)
-          load_pair(st[u], (isv ? Vbh : Kbh) + tok * D + 8 * o, D);
-        else
-          zero_pair(st[u]);
+    for (int j = 0; j < kIssues; ++j) {
+      const int rr = kRowsPerWave * wv + kRPI * j + lane / RT::kUnits;
+      uint32_t tok = (uint32_t)(cb * kChunk + (rr & (kChunk - 1)));
+      if (ti < kLocalTiles) {
+        tok += (uint32_t)(ti * TK);
+      } else {
+        const int slot = kGroupsPerTile * (ti - kLocalTiles) + (rr >> 3);
+        if (slot < nvalid) tok = (uint32_t)(s_glist[slot] * kGroup + (rr & 7));
       }
+      off[j] = dma_offset<T, D>(rr, tok);
     }
-  };
-  auto store_tile = [&](char* buf) {
 #pragma unroll
-    for (int u = 0; u < Cfg::kJobsPerThread; ++u) {
-      const int job = tid + kThreads * u;
-      if (job < Cfg::kJobs) {
-        const bool isv = job >= Cfg::kPairs;
-        const int pr = isv ? job - Cfg::kPairs : job;
-        const int q = pr / (D / 8), o = pr % (D / 8);
-        if (isv) {
-          store_pair_rows<D>(buf + RT::kBytes, st[u], q, o);
-        } else {
-          store_pair_rows<D>(buf, st[u], q, o);
-          store_pair_cols<D>(buf + 2 * RT::kBytes, st[u], q, o);
-        }
-      }
+    for (int j = 0; j < kIssues; ++j) {
+      const uint32_t dst = buf + (uint32_t)((kRowsPerWave * wv + kRPI * j) * RT::kUnits * 16);
+      dma16_off(off[j], Kbh, dst);
+      dma16_off(off[j], Vbh, dst + kTileBytes);
     }
   };
 
@@ -160,61 +191,83 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dq_kernel(const DqP p) {
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) dqacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_tile(0);
-  store_tile(smem);
-  __syncthreads();
-  for (int ti = 0; ti < ntiles; ++ti) {
-    if (ti + 1 < ntiles) load_tile(ti + 1);
-    const char* buf = smem + (Cfg::kStages == 2 ? (ti & 1) : 0) * Cfg::kStage;
-    const char* vs = buf + RT::kBytes;
-    const char* kt = buf + 2 * RT::kBytes;
-
-    f32x4 sacc[4], dpacc[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+  for (int ti = 0; ti < S - 1; ++ti)
+    if (ti < ntiles) issue(ti);
+
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int ahead = (ntiles - 1 - ti) < (S - 2) ? (ntiles - 1 - ti) : (S - 2);
+    if (ahead >= 2) wait_vmcnt<2 * kLoads>();
+    else if (ahead == 1) wait_vmcnt<kLoads>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (ti + S - 1 < ntiles) issue(ti + S - 1);
+
+    const char* kt = smem + (ti % S) * kStage;
+    const char* vt = kt + kTileBytes;
+
+    f32x4 sacc[NKS], dpacc[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
       sacc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
       dpacc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
         Frag<T> a;
-        frag_rows<T, D>(a, buf, 16 * ks + l16, s, g4);
+        frag_rows<T, D>(a, kt, 16 * ks + l16, s, g4);
         mma(sacc[ks], a, qf[s]);
-        frag_rows<T, D>(a, vs, 16 * ks + l16, s, g4);
+        frag_rows<T, D>(a, vt, 16 * ks + l16, s, g4);
         mma(dpacc[ks], a, dof[s]);
       }
     }
+    if (ti < kLocalTiles) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bool gvalid = true;
-      if (ti > 0) {
-        const int slot = 8 * (ti - 1) + 2 * ks + (g4 >> 1);
-        gvalid = slot < p.top_g && s_glist[slot] >= 0;
-      }
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = 16 * ks + 4 * g4 + i;
-        const bool valid = ti == 0 ? kk <= qq : gvalid;
-        const float pr = valid ? __builtin_amdgcn_exp2f(sacc[ks][i] * c2 - lse2) : 0.f;
-        sacc[ks][i] = pr * (dpacc[ks][i] - delta);   // dS
+        for (int i = 0; i < 4; ++i)
+          if (TK * ti + 16 * ks + 4 * g4 + i > qq) sacc[ks][i] = -INFINITY;
+    } else if (kGroupsPerTile * (ti - kLocalTiles + 1) > nvalid) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int slot = kGroupsPerTile * (ti - kLocalTiles) + 2 * ks + (g4 >> 1);
+        if (slot >= nvalid) sacc[ks] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       }
     }
-    Frag<T> dsf[2];
-    frag_from_acc(dsf[0], sacc[0], sacc[1]);
-    frag_from_acc(dsf[1], sacc[2], sacc[3]);
 #pragma unroll
-    for (int dd = 0; dd < D / 16; ++dd)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        Frag<T> a;
-        frag_cols<T, D>(a, kt, 16 * dd + l16, mm, g4);
-        mma(dqacc[dd], a, dsf[mm]);
+      for (int i = 0; i < 4; ++i) {
+        const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[ks][i], c2, nlse2));
+        sacc[ks][i] = pr * (dpacc[ks][i] - delta);   // dS
       }
+    Frag<T> dsf[NMM];
+#pragma unroll
+    for (int mm = 0; mm < NMM; ++mm) frag_from_acc(dsf[mm], sacc[2 * mm], sacc[2 * mm + 1]);
 
-    if (Cfg::kStages == 1) __syncthreads();
-    if (ti + 1 < ntiles) store_tile(smem + (Cfg::kStages == 2 ? ((ti + 1) & 1) : 0) * Cfg::kStage);
-    __syncthreads();
+    // dQ^T += K^T . dS^T ; K^T items of key slice mm: keys 32mm+4g+t, 32mm+16+4g+t
+    constexpr int NF = (D / 16) * NMM;
+#pragma unroll
+    for (int f0 = 0; f0 < NF; f0 += 4) {
+      int ra[4], rb[4], cbk[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = f0 + i, ds = f / NMM, mm = f % NMM;
+        ra[i] = 32 * mm + 4 * g4 + (sizeof(T) == 2 ? (l16 >> 2) : 0);
+        rb[i] = ra[i] + 16;
+        cbk[i] = ds;
+      }
+      Frag<T> kf[4];
+      tr_frags<T, D>(kf, kt, ra, rb, cbk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = f0 + i, ds = f / NMM, mm = f % NMM;
+        mma(dqacc[ds], kf[i], dsf[mm]);
+      }
+    }
   }
 
+  // stores only after the tile pipeline: its vmcnt waits count direct loads only
+  if (g4 == 0) p.delta[qrow0 + qq] = delta;
   T* dq = reinterpret_cast<T*>(p.dQ) + (qrow0 + qq) * D + 4 * g4;
   const float sc = p.scale;
 #pragma unroll
@@ -238,29 +291,19 @@ struct DkvP {
   float scale;
 };
 
-template <typename T, int D> struct DkvCfg {
-  using RT = RowTile<T, D>;
-  using CT = ColTile<T, D>;
-  // stage: Q rows | dO rows | Q transposed | dO transposed | lse2[64] | delta[64]
-  static constexpr int kOffDo = RT::kBytes;
-  static constexpr int kOffQt = 2 * RT::kBytes;
-  static constexpr int kOffDot = 2 * RT::kBytes + CT::kBytes;
-  static constexpr int kOffStat = 2 * RT::kBytes + 2 * CT::kBytes;
-  static constexpr int kStage = kOffStat + 2 * 64 * 4;
-  static constexpr int kStages = 2 * kStage <= 142 * 1024 ? 2 : 1;
-  static constexpr int kPairs = 16 * (D / 8);
-  static constexpr int kJobs = 2 * kPairs;      // Q pairs, then dO pairs
-  static constexpr int kJobsPerThread = (kJobs + kThreads - 1) / kThreads;
-};
-
 // entry word: (row << 9) | mask, mask bits 0..7 = kept groups, bit 8 = own chunk
 constexpr uint32_t kLocalBit = 1u << 8;
 
-template <typename T, int D>
+template <typename T, int D, int S>
 __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p) {
-  using Cfg = DkvCfg<T, D>;
-  using RT = typename Cfg::RT;
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::kStages * Cfg::kStage];
+  using RT = RowTile<T, D>;
+  constexpr int kTileBytes = 64 * RT::kUnits * 16;                // 64 query rows
+  constexpr int kStatBytes = 4 * 128;                             // per wave: 16 lse, 16 delta
+  constexpr int kStage = 2 * kTileBytes + kStatBytes;             // Q | dO | stats
+  constexpr int kRPI = rows_per_issue<T, D>();
+  constexpr int kIssues = 16 / kRPI;                              // per matrix per wave
+  constexpr int kLoads = 2 * kIssues + 1;                         // + the stats load
+  __shared__ __attribute__((aligned(1024))) char smem[S * kStage];
   __shared__ uint32_t s_ent[kRowsPerPass];
   __shared__ int s_wsum[4];
 
@@ -273,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
   const int r = p.Hq / p.Hkv;
   const int nrows = r * p.nblk;          // (query head in group, block), head-major
   const int kin = 16 * wv + l16;         // this lane's key within the chunk
-  const int mygroups = 3 << (2 * wv);    // the two groups owned by this wavefront
+  const uint32_t mygroups = 3u << (2 * wv);
 
   // this wavefront's 16 keys as B operands of S = Q . K^T and dP = dO . V^T
   Frag<T> kf[D / 32], vf[D / 32];
@@ -296,46 +339,28 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
   const float c2 = p.scale * kLog2e;
   const int blk_first = c - p.q0 / kChunk;   // rows with block >= this can touch chunk c
 
-  Pair<T> st[Cfg::kJobsPerThread];
-  float st_stat = 0.f;
-  auto entry_rows = [&](uint32_t ent, int& hq, int& blk) {
-    const int rr = (int)(ent >> 9);
-    hq = hkv * r + rr / p.nblk;
-    blk = rr % p.nblk;
-  };
-  auto load_entry = [&](uint32_t ent) {
-    int hq, blk;
-    entry_rows(ent, hq, blk);
+  const uint32_t smem_lds = lds_addr(smem);
+  // Q rows, dO rows (16 per wave) and this wave's 16 lse / delta values
+  auto issue = [&](uint32_t ent, int slot) {
+    const int rr0 = (int)(ent >> 9);
+    const int hq = hkv * r + rr0 / p.nblk, blk = rr0 % p.nblk;
     const long long qrow0 = ((long long)b * p.Hq + hq) * p.Sq + (long long)blk * kChunk;
+    const T* qb = reinterpret_cast<const T*>(p.Q) + qrow0 * D;
+    const T* ob = reinterpret_cast<const T*>(p.dO) + qrow0 * D;
+    const uint32_t buf = smem_lds + (uint32_t)(slot * kStage);
 #pragma unroll
-    for (int u = 0; u < Cfg::kJobsPerThread; ++u) {
-      const int job = tid + kThreads * u;
-      if (job < Cfg::kJobs) {
-        const bool isdo = job >= Cfg::kPairs;
-        const int pr = isdo ? job - Cfg::kPairs : job;
-        const int q = pr / (D / 8), o = pr % (D / 8);
-        const T* src = reinterpret_cast<const T*>(isdo ? p.dO : p.Q) + (qrow0 + 4 * q) * D + 8 * o;
-        load_pair(st[u], src, D);
-      }
+    for (int j = 0; j < kIssues; ++j) {
+      const int rr = 16 * wv + kRPI * j + lane / RT::kUnits;
+      const uint32_t off = dma_offset<T, D>(rr, (uint32_t)rr);
+      const uint32_t dst = buf + (uint32_t)((16 * wv + kRPI * j) * RT::kUnits * 16);
+      dma16_off(off, qb, dst);
+      dma16_off(off, ob, dst + kTileBytes);
     }
-    if (tid < 64)
-      st_stat = p.lse[qrow0 + tid] * kLog2e;
-    else if (tid < 128)
-      st_stat = p.delta[qrow0 + tid - 64];
-  };
-  auto store_entry = [&](char* buf) {
-#pragma unroll
-    for (int u = 0; u < Cfg::kJobsPerThread; ++u) {
-      const int job = tid + kThreads * u;
-      if (job < Cfg::kJobs) {
-        const bool isdo = job >= Cfg::kPairs;
-        const int pr = isdo ? job - Cfg::kPairs : job;
-        const int q = pr / (D / 8), o = pr % (D / 8);
-        store_pair_rows<D>(buf + (isdo ? Cfg::kOffDo : 0), st[u], q, o);
-        store_pair_cols<D>(buf + (isdo ? Cfg::kOffDot : Cfg::kOffQt), st[u], q, o);
-      }
+    // lanes 0..3: lse of queries 16w..16w+15, lanes 4..7: delta of the same
+    if (lane < 8) {
+      const float* src = (lane < 4 ? p.lse : p.delta) + qrow0 + 16 * wv + 4 * (lane & 3);
+      dma16(src, buf + (uint32_t)(2 * kTileBytes + 128 * wv));
     }
-    if (tid < 128) reinterpret_cast<float*>(buf + Cfg::kOffStat)[tid] = st_stat;
   };
 
   for (int r0 = 0; r0 < nrows; r0 += kRowsPerPass) {
@@ -381,20 +406,24 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
     }
     if (nent == 0) continue;
 
-    // ---- walk the entries
-    load_entry(s_ent[0]);
-    store_entry(smem);
-    __syncthreads();
+    // ---- walk the entries, S - 1 of them in flight
+#pragma unroll
+    for (int e = 0; e < S - 1; ++e)
+      if (e < nent) issue(s_ent[e], e % S);
     for (int e = 0; e < nent; ++e) {
-      if (e + 1 < nent) load_entry(s_ent[e + 1]);
-      const char* buf = smem + (Cfg::kStages == 2 ? (e & 1) : 0) * Cfg::kStage;
+      const int ahead = (nent - 1 - e) < (S - 2) ? (nent - 1 - e) : (S - 2);
+      if (ahead >= 2) wait_vmcnt<2 * kLoads>();
+      else if (ahead == 1) wait_vmcnt<kLoads>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (e + S - 1 < nent) issue(s_ent[e + S - 1], (e + S - 1) % S);
+
       const uint32_t ent = s_ent[e];
       const bool local = (ent & kLocalBit) != 0;
       if (local || (ent & mygroups)) {
-        const char* dos = buf + Cfg::kOffDo;
-        const char* qt = buf + Cfg::kOffQt;
-        const char* dot = buf + Cfg::kOffDot;
-        const float* stat = reinterpret_cast<const float*>(buf + Cfg::kOffStat);
+        const char* qt = smem + (e % S) * kStage;
+        const char* ot = qt + kTileBytes;
+        const float* stat = reinterpret_cast<const float*>(qt + 2 * kTileBytes);
         const bool kvalid = local || ((ent >> (kin >> 3)) & 1u);
 
         f32x4 sacc[4], dpacc[4];
@@ -405,23 +434,24 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
 #pragma unroll
           for (int s = 0; s < D / 32; ++s) {
             Frag<T> a;
-            frag_rows<T, D>(a, buf, 16 * qs + l16, s, g4);
+            frag_rows<T, D>(a, qt, 16 * qs + l16, s, g4);
             mma(sacc[qs], a, kf[s]);
-            frag_rows<T, D>(a, dos, 16 * qs + l16, s, g4);
+            frag_rows<T, D>(a, ot, 16 * qs + l16, s, g4);
             mma(dpacc[qs], a, vf[s]);
           }
         }
 #pragma unroll
         for (int qs = 0; qs < 4; ++qs) {
-          const float4 l4 = reinterpret_cast<const float4*>(stat)[4 * qs + g4];
-          const float4 d4 = reinterpret_cast<const float4*>(stat + 64)[4 * qs + g4];
+          // queries 16qs + 4g + i: stats of wave-slot qs at [lse 16 | delta 16]
+          const float4 l4 = reinterpret_cast<const float4*>(stat + 32 * qs)[g4];
+          const float4 d4 = reinterpret_cast<const float4*>(stat + 32 * qs + 16)[g4];
           const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
           const float dq[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int q = 16 * qs + 4 * g4 + i;
             const bool valid = local ? kin <= q : kvalid;
-            const float pr = valid ? __builtin_amdgcn_exp2f(sacc[qs][i] * c2 - lq[i]) : 0.f;
+            const float pr = valid ? __builtin_amdgcn_exp2f(fmaf(sacc[qs][i], c2, -lq[i] * kLog2e)) : 0.f;
             sacc[qs][i] = pr;
             dpacc[qs][i] = pr * (dpacc[qs][i] - dq[i]);
           }
@@ -431,21 +461,30 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
         frag_from_acc(pf[1], sacc[2], sacc[3]);
         frag_from_acc(dsf[0], dpacc[0], dpacc[1]);
         frag_from_acc(dsf[1], dpacc[2], dpacc[3]);
+        // dV^T += dO^T . P and dK^T += Q^T . dS; the transposed operands cover
+        // queries 32mm+4g+t, 32mm+16+4g+t of column block dd
 #pragma unroll
-        for (int dd = 0; dd < D / 16; ++dd)
+        for (int dd = 0; dd < D / 16; dd += 2) {
+          int ra[4], rb[4], cbk[4];
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
-            Frag<T> a;
-            frag_cols<T, D>(a, dot, 16 * dd + l16, mm, g4);
-            mma(dvacc[dd], a, pf[mm]);
-            frag_cols<T, D>(a, qt, 16 * dd + l16, mm, g4);
-            mma(dkacc[dd], a, dsf[mm]);
+          for (int i = 0; i < 4; ++i) {
+            const int mm = i & 1;
+            ra[i] = 32 * mm + 4 * g4 + (sizeof(T) == 2 ? (l16 >> 2) : 0);
+            rb[i] = ra[i] + 16;
+            cbk[i] = dd + (i >> 1);
           }
+          Frag<T> fo[4], fq[4];
+          tr_frags<T, D>(fo, ot, ra, rb, cbk);
+          tr_frags<T, D>(fq, qt, ra, rb, cbk);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            mma(dvacc[dd + (i >> 1)], fo[i], pf[i & 1]);
+            mma(dkacc[dd + (i >> 1)], fq[i], dsf[i & 1]);
+          }
+        }
       }
-      if (Cfg::kStages == 1) __syncthreads();
-      if (e + 1 < nent) store_entry(smem + (Cfg::kStages == 2 ? ((e + 1) & 1) : 0) * Cfg::kStage);
-      __syncthreads();
     }
+    __syncthreads();   // the entry list and stage buffers are reused by the next pass
   }
 
   // every key of the chunk is written (zero when nothing attends it)
@@ -470,7 +509,12 @@ hipError_t run_dq(const Dims& d, const void* Q, const void* K, const void* V, co
   p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.q0 = d.q0;
   p.nblk = d.nblk; p.top_g = d.top_g; p.scale = d.scale;
   p.nwork = d.B * d.Hq * d.nblk;
-  attend_bwd_dq_kernel<T, D><<<p.nwork, kThreads, 0, s>>>(p);
+  constexpr int TK = HGA_DQ_TILE;
+  constexpr int kStageBytes = 2 * TK * D * (int)sizeof(T);
+  constexpr int S0 = HGA_DQ_STAGES;
+  constexpr int S = S0 * kStageBytes <= 128 * 1024 ? S0 : (128 * 1024) / kStageBytes;
+  static_assert(S >= 2, "at least two stages");
+  attend_bwd_dq_kernel<T, D, TK, S><<<p.nwork, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -485,7 +529,11 @@ hipError_t run_dkdv(const Dims& d, const void* Q, const void* K, const void* V, 
   p.nblk = d.nblk; p.top_g = d.top_g; p.scale = d.scale;
   p.nchunks = d.Skv / kChunk;
   p.nwork = d.B * d.Hkv * p.nchunks;
-  attend_bwd_dkdv_kernel<T, D><<<p.nwork, kThreads, 0, s>>>(p);
+  constexpr int kStageBytes = 2 * 64 * D * (int)sizeof(T) + 512;
+  constexpr int S0 = HGA_DKV_STAGES;
+  constexpr int S = S0 * kStageBytes <= 140 * 1024 ? S0 : (140 * 1024) / kStageBytes;
+  static_assert(S >= 2, "at least two stages");
+  attend_bwd_dkdv_kernel<T, D, S><<<p.nwork, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
