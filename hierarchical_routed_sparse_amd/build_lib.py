@@ -33,21 +33,23 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, extra, build_dir=BUILD) -> str:
+def _compile(src: str, extra, build_dir=BUILD, csrc=CSRC) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(csrc, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False, extra=(), out: str = LIB, build_dir: str = BUILD) -> str:
+def build(verbose: bool = False, extra=(), out: str = LIB, build_dir: str = BUILD,
+          csrc: str = CSRC) -> str:
     """Compiles every HIP source and links libhga.so (or `out`); returns its path.
-    `extra` holds additional hipcc flags, e.g. -D overrides of tuning constants."""
+    `extra` holds additional hipcc flags, e.g. -D overrides of tuning constants;
+    `csrc` may point at another copy of the sources."""
     os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra), build_dir), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, list(extra), build_dir, csrc), SOURCES))
     tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

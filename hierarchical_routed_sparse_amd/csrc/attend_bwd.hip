@@ -67,26 +67,6 @@ __device__ __forceinline__ int load_routing_row(const int32_t* grow, int top_g, 
   return nvalid;
 }
 
-// 8 operand fragments of a transposed read of tile rows: fragment f covers
-// column block cbk[f] and row bases rows (ra[f], rb[f]) as in frag_tr.
-template <typename T, int D>
-__device__ __forceinline__ void tr_frags(Frag<T> (&out)[4], const char* tile, const int (&ra)[4],
-                                         const int (&rb)[4], const int (&cbk)[4]) {
-  if constexpr (sizeof(T) == 2) {
-    const uint32_t base = lds_addr(tile);
-    uint32_t a[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[2 * i] = tr_base<D>(base, ra[i]) ^ (uint32_t)(32 * cbk[i]);
-      a[2 * i + 1] = tr_base<D>(base, rb[i]) ^ (uint32_t)(32 * cbk[i]);
-    }
-    tr_frags4(out, a);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) frag_tr<T, D>(out[i], tile, ra[i], rb[i], 16 * cbk[i]);
-  }
-}
-
 // ============================================================== dQ
 
 struct DqP {
@@ -163,21 +143,35 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dq_kernel(const DqP p) {
   const float nlse2 = -p.lse[qrow0 + qq] * kLog2e;
   const float c2 = p.scale * kLog2e;
 
+  // loop-invariant per-lane offsets (see attend_fwd.hip)
+  RowOffsets<T, D> kro;
+  kro.init();
+  TrOffsets<(sizeof(T) == 2 ? D : 16)> kto;
+  if constexpr (sizeof(T) == 2) kto.init();
+  int ld_row[kIssues];
+  uint32_t ld_col[kIssues];
+#pragma unroll
+  for (int j = 0; j < kIssues; ++j) {
+    ld_row[j] = kRowsPerWave * wv + kRPI * j + lane / RT::kUnits;
+    ld_col[j] = (uint32_t)(((lane % RT::kUnits) ^ RT::swz(ld_row[j])) << 4);
+  }
+
   const uint32_t smem_lds = lds_addr(smem);
   auto issue = [&](int ti) {
     const uint32_t buf = smem_lds + (uint32_t)((ti % S) * kStage);
     uint32_t off[kIssues];
 #pragma unroll
     for (int j = 0; j < kIssues; ++j) {
-      const int rr = kRowsPerWave * wv + kRPI * j + lane / RT::kUnits;
+      const int rr = ld_row[j];
       uint32_t tok = (uint32_t)(cb * kChunk + (rr & (kChunk - 1)));
       if (ti < kLocalTiles) {
         tok += (uint32_t)(ti * TK);
       } else {
         const int slot = kGroupsPerTile * (ti - kLocalTiles) + (rr >> 3);
-        if (slot < nvalid) tok = (uint32_t)(s_glist[slot] * kGroup + (rr & 7));
+        const int gm = s_glist[slot < kMaxTopG ? slot : kMaxTopG - 1];
+        tok = slot < nvalid ? (uint32_t)(gm * kGroup + (rr & 7)) : tok;
       }
-      off[j] = dma_offset<T, D>(rr, tok);
+      off[j] = tok * (uint32_t)(RT::kUnits * 16) + ld_col[j];
     }
 #pragma unroll
     for (int j = 0; j < kIssues; ++j) {
@@ -206,17 +200,22 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dq_kernel(const DqP p) {
     const char* kt = smem + (ti % S) * kStage;
     const char* vt = kt + kTileBytes;
 
+    constexpr int RB = RT::kUnits * 16;
     f32x4 sacc[NKS], dpacc[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       sacc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
       dpacc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
+    for (int s = 0; s < D / 32; ++s) {
+      const char* kp = kt + kro.o[s];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
         Frag<T> a;
-        frag_rows<T, D>(a, kt, 16 * ks + l16, s, g4);
+        frag_rows_at<T, D>(a, kp + 16 * ks * RB);
         mma(sacc[ks], a, qf[s]);
-        frag_rows<T, D>(a, vt, 16 * ks + l16, s, g4);
+        frag_rows_at<T, D>(a, kp + kTileBytes + 16 * ks * RB);
         mma(dpacc[ks], a, dof[s]);
       }
     }
@@ -245,24 +244,41 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dq_kernel(const DqP p) {
     for (int mm = 0; mm < NMM; ++mm) frag_from_acc(dsf[mm], sacc[2 * mm], sacc[2 * mm + 1]);
 
     // dQ^T += K^T . dS^T ; K^T items of key slice mm: keys 32mm+4g+t, 32mm+16+4g+t
-    constexpr int NF = (D / 16) * NMM;
+    if constexpr (sizeof(T) == 2) {
+      uint32_t ka[D / 16];
 #pragma unroll
-    for (int f0 = 0; f0 < NF; f0 += 4) {
-      int ra[4], rb[4], cbk[4];
+      for (int c = 0; c < D / 16; ++c) ka[c] = lds_addr(kt) + kto.o[c];
+      if constexpr (NMM == 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = f0 + i, ds = f / NMM, mm = f % NMM;
-        ra[i] = 32 * mm + 4 * g4 + (sizeof(T) == 2 ? (l16 >> 2) : 0);
-        rb[i] = ra[i] + 16;
-        cbk[i] = ds;
+        for (int c = 0; c < D / 16; c += 4) {
+          const uint32_t a[8] = {ka[c], ka[c], ka[c + 1], ka[c + 1],
+                                 ka[c + 2], ka[c + 2], ka[c + 3], ka[c + 3]};
+          Frag<T> kf[4];
+          tr_read8_sched<0, 16 * RB, 0, 16 * RB, 0, 16 * RB, 0, 16 * RB>(kf, a);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mma(dqacc[c + i], kf[i], dsf[0]);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < D / 16; c += 2) {
+          const uint32_t a[8] = {ka[c], ka[c], ka[c], ka[c], ka[c + 1], ka[c + 1], ka[c + 1], ka[c + 1]};
+          Frag<T> kf[4];
+          tr_read8_sched<0, 16 * RB, 32 * RB, 48 * RB, 0, 16 * RB, 32 * RB, 48 * RB>(kf, a);
+          mma(dqacc[c], kf[0], dsf[0]);
+          mma(dqacc[c], kf[1], dsf[1]);
+          mma(dqacc[c + 1], kf[2], dsf[0]);
+          mma(dqacc[c + 1], kf[3], dsf[1]);
+        }
       }
-      Frag<T> kf[4];
-      tr_frags<T, D>(kf, kt, ra, rb, cbk);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = f0 + i, ds = f / NMM, mm = f % NMM;
-        mma(dqacc[ds], kf[i], dsf[mm]);
-      }
+      for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+        for (int mm = 0; mm < NMM; ++mm) {
+          Frag<T> kf;
+          frag_tr<T, D>(kf, kt, 32 * mm + 4 * g4, 32 * mm + 16 + 4 * g4, 16 * ds);
+          mma(dqacc[ds], kf, dsf[mm]);
+        }
     }
   }
 
@@ -294,10 +310,43 @@ struct DkvP {
 // entry word: (row << 9) | mask, mask bits 0..7 = kept groups, bit 8 = own chunk
 constexpr uint32_t kLocalBit = 1u << 8;
 
+// Group mask of chunk c in one ascending, -1 padded routing row g[0..top_g):
+// bit t set when group 8c+t is kept.  Two rounds of independent loads: 16
+// evenly spaced samples bracket the position of the first group >= 8c, then
+// the bracket plus the 8 slots after it are read.
+__device__ __forceinline__ uint32_t chunk_mask(const int32_t* g, int top_g, int c) {
+  const int lo_g = 8 * c;
+  const int stride = (top_g + 15) >> 4;
+  int below = 0;   // samples holding a valid group below chunk c
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int idx = i * stride;
+    const int v = idx < top_g ? g[idx] : -1;
+    below += (v >= 0 && v < lo_g) ? 1 : 0;
+  }
+  // every entry before sample `below - 1` is below chunk c; chunk c's groups
+  // (at most 8) start in [lo, lo + stride]
+  const int lo = below > 0 ? (below - 1) * stride : 0;
+  uint32_t mask = 0;
+  for (int i0 = 0; i0 < stride + 8; i0 += 16) {
+    int v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int idx = lo + i0 + i;
+      v[i] = (i0 + i < stride + 8 && idx < top_g) ? g[idx] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (v[i] >= lo_g && v[i] < lo_g + 8) mask |= 1u << (v[i] - lo_g);
+  }
+  return mask;
+}
+
 template <typename T, int D, int S>
 __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p) {
   using RT = RowTile<T, D>;
-  constexpr int kTileBytes = 64 * RT::kUnits * 16;                // 64 query rows
+  constexpr int RB = RT::kUnits * 16;
+  constexpr int kTileBytes = 64 * RB;                             // 64 query rows
   constexpr int kStatBytes = 4 * 128;                             // per wave: 16 lse, 16 delta
   constexpr int kStage = 2 * kTileBytes + kStatBytes;             // Q | dO | stats
   constexpr int kRPI = rows_per_issue<T, D>();
@@ -339,6 +388,18 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
   const float c2 = p.scale * kLog2e;
   const int blk_first = c - p.q0 / kChunk;   // rows with block >= this can touch chunk c
 
+  // loop-invariant per-lane offsets (see attend_fwd.hip)
+  RowOffsets<T, D> qro;
+  qro.init();
+  TrOffsets<(sizeof(T) == 2 ? D : 16)> qto;
+  if constexpr (sizeof(T) == 2) qto.init();
+  uint32_t ld_off[kIssues];
+#pragma unroll
+  for (int j = 0; j < kIssues; ++j) {
+    const int rr = 16 * wv + kRPI * j + lane / RT::kUnits;
+    ld_off[j] = (uint32_t)(rr * RB) + (uint32_t)(((lane % RT::kUnits) ^ RT::swz(rr)) << 4);
+  }
+
   const uint32_t smem_lds = lds_addr(smem);
   // Q rows, dO rows (16 per wave) and this wave's 16 lse / delta values
   auto issue = [&](uint32_t ent, int slot) {
@@ -350,11 +411,9 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
     const uint32_t buf = smem_lds + (uint32_t)(slot * kStage);
 #pragma unroll
     for (int j = 0; j < kIssues; ++j) {
-      const int rr = 16 * wv + kRPI * j + lane / RT::kUnits;
-      const uint32_t off = dma_offset<T, D>(rr, (uint32_t)rr);
-      const uint32_t dst = buf + (uint32_t)((16 * wv + kRPI * j) * RT::kUnits * 16);
-      dma16_off(off, qb, dst);
-      dma16_off(off, ob, dst + kTileBytes);
+      const uint32_t dst = buf + (uint32_t)((16 * wv + kRPI * j) * RB);
+      dma16_off(ld_off[j], qb, dst);
+      dma16_off(ld_off[j], ob, dst + kTileBytes);
     }
     // lanes 0..3: lse of queries 16w..16w+15, lanes 4..7: delta of the same
     if (lane < 8) {
@@ -374,19 +433,8 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
         if (blk == blk_first) {
           mask = kLocalBit | 0xFFu;
         } else if (blk > blk_first) {
-          const int32_t* g = p.gidx + (((long long)b * p.Hq + hq) * p.nblk + blk) * p.top_g;
-          const int lo_g = 8 * c;
-          int lo = 0, hi = p.top_g;      // first entry that is not a valid group below chunk c
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            const int v = g[mid];
-            if (v >= 0 && v < lo_g) lo = mid + 1; else hi = mid;
-          }
-          for (int i = lo; i < p.top_g && i < lo + 8; ++i) {
-            const int v = g[i];
-            if (v < lo_g || v >= lo_g + 8) break;
-            mask |= 1u << (v - lo_g);
-          }
+          mask = chunk_mask(p.gidx + (((long long)b * p.Hq + hq) * p.nblk + blk) * p.top_g,
+                            p.top_g, c);
         }
       }
       const bool f = mask != 0;
@@ -422,24 +470,29 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
       const bool local = (ent & kLocalBit) != 0;
       if (local || (ent & mygroups)) {
         const char* qt = smem + (e % S) * kStage;
-        const char* ot = qt + kTileBytes;
         const float* stat = reinterpret_cast<const float*>(qt + 2 * kTileBytes);
-        const bool kvalid = local || ((ent >> (kin >> 3)) & 1u);
 
         f32x4 sacc[4], dpacc[4];
 #pragma unroll
         for (int qs = 0; qs < 4; ++qs) {
           sacc[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
           dpacc[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-          for (int s = 0; s < D / 32; ++s) {
+        for (int s = 0; s < D / 32; ++s) {
+          const char* qp = qt + qro.o[s];
+#pragma unroll
+          for (int qs = 0; qs < 4; ++qs) {
             Frag<T> a;
-            frag_rows<T, D>(a, qt, 16 * qs + l16, s, g4);
+            frag_rows_at<T, D>(a, qp + 16 * qs * RB);
             mma(sacc[qs], a, kf[s]);
-            frag_rows<T, D>(a, ot, 16 * qs + l16, s, g4);
+            frag_rows_at<T, D>(a, qp + kTileBytes + 16 * qs * RB);
             mma(dpacc[qs], a, vf[s]);
           }
         }
+        // P (zero for unattended pairs) and dS; a key outside the row's kept
+        // groups gets lse = +inf, so P = exp2(-inf) = 0
+        const bool kvalid = local || ((ent >> (kin >> 3)) & 1u);
 #pragma unroll
         for (int qs = 0; qs < 4; ++qs) {
           // queries 16qs + 4g + i: stats of wave-slot qs at [lse 16 | delta 16]
@@ -449,9 +502,9 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
           const float dq[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int q = 16 * qs + 4 * g4 + i;
-            const bool valid = local ? kin <= q : kvalid;
-            const float pr = valid ? __builtin_amdgcn_exp2f(fmaf(sacc[qs][i], c2, -lq[i] * kLog2e)) : 0.f;
+            const float nl = kvalid ? -lq[i] * kLog2e : -INFINITY;
+            float pr = __builtin_amdgcn_exp2f(fmaf(sacc[qs][i], c2, nl));
+            if (local && kin > 16 * qs + 4 * g4 + i) pr = 0.f;
             sacc[qs][i] = pr;
             dpacc[qs][i] = pr * (dpacc[qs][i] - dq[i]);
           }
@@ -462,25 +515,40 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
         frag_from_acc(dsf[0], dpacc[0], dpacc[1]);
         frag_from_acc(dsf[1], dpacc[2], dpacc[3]);
         // dV^T += dO^T . P and dK^T += Q^T . dS; the transposed operands cover
-        // queries 32mm+4g+t, 32mm+16+4g+t of column block dd
+        // queries 32mm+4g+t, 32mm+16+4g+t of column block cb
+        if constexpr (sizeof(T) == 2) {
+          uint32_t qa[D / 16];
 #pragma unroll
-        for (int dd = 0; dd < D / 16; dd += 2) {
-          int ra[4], rb[4], cbk[4];
+          for (int cc = 0; cc < D / 16; ++cc) qa[cc] = lds_addr(qt) + qto.o[cc];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int mm = i & 1;
-            ra[i] = 32 * mm + 4 * g4 + (sizeof(T) == 2 ? (l16 >> 2) : 0);
-            rb[i] = ra[i] + 16;
-            cbk[i] = dd + (i >> 1);
+          for (int cc = 0; cc < D / 16; cc += 2) {
+            const uint32_t a[8] = {qa[cc], qa[cc], qa[cc], qa[cc],
+                                   qa[cc + 1], qa[cc + 1], qa[cc + 1], qa[cc + 1]};
+            Frag<T> fo[4], fq[4];
+            tr_read8_sched<kTileBytes, kTileBytes + 16 * RB, kTileBytes + 32 * RB, kTileBytes + 48 * RB,
+                         kTileBytes, kTileBytes + 16 * RB, kTileBytes + 32 * RB, kTileBytes + 48 * RB>(fo, a);
+            tr_read8_sched<0, 16 * RB, 32 * RB, 48 * RB, 0, 16 * RB, 32 * RB, 48 * RB>(fq, a);
+            mma(dvacc[cc], fo[0], pf[0]);
+            mma(dvacc[cc], fo[1], pf[1]);
+            mma(dvacc[cc + 1], fo[2], pf[0]);
+            mma(dvacc[cc + 1], fo[3], pf[1]);
+            mma(dkacc[cc], fq[0], dsf[0]);
+            mma(dkacc[cc], fq[1], dsf[1]);
+            mma(dkacc[cc + 1], fq[2], dsf[0]);
+            mma(dkacc[cc + 1], fq[3], dsf[1]);
           }
-          Frag<T> fo[4], fq[4];
-          tr_frags<T, D>(fo, ot, ra, rb, cbk);
-          tr_frags<T, D>(fq, qt, ra, rb, cbk);
+        } else {
+          const char* ot = qt + kTileBytes;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            mma(dvacc[dd + (i >> 1)], fo[i], pf[i & 1]);
-            mma(dkacc[dd + (i >> 1)], fq[i], dsf[i & 1]);
-          }
+          for (int dd = 0; dd < D / 16; ++dd)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+              Frag<T> fo, fq;
+              frag_tr<T, D>(fo, ot, 32 * mm + 4 * g4, 32 * mm + 16 + 4 * g4, 16 * dd);
+              frag_tr<T, D>(fq, qt, 32 * mm + 4 * g4, 32 * mm + 16 + 4 * g4, 16 * dd);
+              mma(dvacc[dd], fo, pf[mm]);
+              mma(dkacc[dd], fq, dsf[mm]);
+            }
         }
       }
     }

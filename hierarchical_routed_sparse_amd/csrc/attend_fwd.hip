@@ -55,7 +55,8 @@ constexpr float kRescale = 8.0f;
 template <typename T, int D, int TK, int S>
 __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
   using RT = RowTile<T, D>;
-  constexpr int kTileBytes = TK * RT::kUnits * 16;                 // one matrix, TK rows
+  constexpr int RB = RT::kUnits * 16;                             // bytes per tile row
+  constexpr int kTileBytes = TK * RB;                             // one matrix, TK rows
   constexpr int kStage = 2 * kTileBytes;                          // K tile | V tile
   constexpr int kRowsPerWave = TK / 4;
   constexpr int kRPI = rows_per_issue<T, D>();
@@ -116,6 +117,20 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
     for (int s = 0; s < D / 32; ++s) load_frag(qf[s], q + 32 * s);
   }
 
+  // loop-invariant per-lane offsets: LDS reads of the K rows, transposed reads
+  // of V, and the swizzled column of each row this lane loads
+  RowOffsets<T, D> kro;
+  kro.init();
+  TrOffsets<(sizeof(T) == 2 ? D : 16)> vto;
+  if constexpr (sizeof(T) == 2) vto.init();
+  int ld_row[kIssues];
+  uint32_t ld_col[kIssues];
+#pragma unroll
+  for (int j = 0; j < kIssues; ++j) {
+    ld_row[j] = kRowsPerWave * wv + kRPI * j + lane / RT::kUnits;
+    ld_col[j] = (uint32_t)(((lane % RT::kUnits) ^ RT::swz(ld_row[j])) << 4);
+  }
+
   // Tiles 0..kLocalTiles-1 cover the own chunk; later tiles hold
   // kGroupsPerTile kept groups.  A slot past the last kept group reads the own
   // chunk (any valid row works: its scores are masked, its P is exactly zero).
@@ -125,19 +140,20 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
     uint32_t off[kIssues];
 #pragma unroll
     for (int j = 0; j < kIssues; ++j) {
-      const int rr = kRowsPerWave * wv + kRPI * j + lane / RT::kUnits;
+      const int rr = ld_row[j];
       uint32_t tok = (uint32_t)(cb * kChunk + (rr & (kChunk - 1)));
       if (ti < kLocalTiles) {
         tok += (uint32_t)(ti * TK);
       } else {
         const int slot = kGroupsPerTile * (ti - kLocalTiles) + (rr >> 3);
-        if (slot < nvalid) tok = (uint32_t)(s_glist[slot] * kGroup + (rr & 7));
+        const int gm = s_glist[slot < kMaxTopG ? slot : kMaxTopG - 1];
+        tok = slot < nvalid ? (uint32_t)(gm * kGroup + (rr & 7)) : tok;
       }
-      off[j] = dma_offset<T, D>(rr, tok);
+      off[j] = tok * (uint32_t)RB + ld_col[j];
     }
 #pragma unroll
     for (int j = 0; j < kIssues; ++j) {
-      const uint32_t dst = buf + (uint32_t)((kRowsPerWave * wv + kRPI * j) * RT::kUnits * 16);
+      const uint32_t dst = buf + (uint32_t)((kRowsPerWave * wv + kRPI * j) * RB);
       dma16_off(off[j], Kbh, dst);
       dma16_off(off[j], Vbh, dst + kTileBytes);
     }
@@ -170,12 +186,14 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
     // S^T = K . Q^T for NKS subtiles of 16 keys (raw dot products)
     f32x4 sacc[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      sacc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < NKS; ++ks) sacc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
+    for (int s = 0; s < D / 32; ++s) {
+      const char* kp = kt + kro.o[s];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
         Frag<T> kf;
-        frag_rows<T, D>(kf, kt, 16 * ks + l16, s, g4);
+        frag_rows_at<T, D>(kf, kp + 16 * ks * RB);
         mma(sacc[ks], kf, qf[s]);
       }
     }
@@ -223,28 +241,29 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
 #pragma unroll
     for (int mm = 0; mm < NMM; ++mm) frag_from_acc(pf[mm], sacc[2 * mm], sacc[2 * mm + 1]);
     if constexpr (sizeof(T) == 2) {
-      const uint32_t vbase = lds_addr(vt);
-      uint32_t rb[2 * NMM];   // (mm, half): rows 32mm + 16h + 4g + (l16 >> 2)
+      uint32_t va[D / 16];
 #pragma unroll
-      for (int mm = 0; mm < NMM; ++mm)
+      for (int c = 0; c < D / 16; ++c) va[c] = lds_addr(vt) + vto.o[c];
+      if constexpr (NMM == 1) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) rb[2 * mm + h] = tr_base<D>(vbase, 32 * mm + 16 * h + 4 * g4 + (l16 >> 2));
-      constexpr int NF = (D / 16) * NMM;   // fragments, index f = ds * NMM + mm
+        for (int c = 0; c < D / 16; c += 4) {
+          const uint32_t a[8] = {va[c], va[c], va[c + 1], va[c + 1],
+                                 va[c + 2], va[c + 2], va[c + 3], va[c + 3]};
+          Frag<T> vf[4];
+          tr_read8_sched<0, 16 * RB, 0, 16 * RB, 0, 16 * RB, 0, 16 * RB>(vf, a);
 #pragma unroll
-      for (int f0 = 0; f0 < NF; f0 += 4) {
-        uint32_t a[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int f = f0 + i, ds = f / NMM, mm = f % NMM;
-          a[2 * i] = rb[2 * mm] ^ (uint32_t)(32 * ds);
-          a[2 * i + 1] = rb[2 * mm + 1] ^ (uint32_t)(32 * ds);
+          for (int i = 0; i < 4; ++i) mma(oacc[c + i], vf[i], pf[0]);
         }
-        Frag<T> vf[4];
-        tr_frags4(vf, a);
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int f = f0 + i, ds = f / NMM, mm = f % NMM;
-          mma(oacc[ds], vf[i], pf[mm]);
+        for (int c = 0; c < D / 16; c += 2) {
+          const uint32_t a[8] = {va[c], va[c], va[c], va[c], va[c + 1], va[c + 1], va[c + 1], va[c + 1]};
+          Frag<T> vf[4];
+          tr_read8_sched<0, 16 * RB, 32 * RB, 48 * RB, 0, 16 * RB, 32 * RB, 48 * RB>(vf, a);
+          mma(oacc[c], vf[0], pf[0]);
+          mma(oacc[c], vf[1], pf[1]);
+          mma(oacc[c + 1], vf[2], pf[0]);
+          mma(oacc[c + 1], vf[3], pf[1]);
         }
       }
     } else {

@@ -76,6 +76,21 @@ __device__ __forceinline__ float xor_sum16_32(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Sum over the wavefront, result in every lane: butterfly over lane xor 1, 2
+// (DPP quad permutes), the two quads of each 8-lane half-row (half-row
+// mirror), the two halves of each 16-lane row (row mirror), then lane xor 16
+// and xor 32 (permlane swaps).  All VALU; no LDS round trip.
+__device__ __forceinline__ int wave_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);  // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = (int)(a[0] + a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return (int)(b[0] + b[1]);
+}
+
 // Work index for block `bid` such that consecutive work indices land on the
 // same XCD.  Workgroups are dispatched round-robin over the 8 XCDs, so XCD x
 // runs bids x, x+8, ...; it receives the contiguous work range
@@ -461,6 +476,115 @@ __device__ __forceinline__ void tr_frags4(Frag<uint16_t> (&f)[4], const uint32_t
   for (int i = 0; i < 4; ++i) {
     f[i].w[0] = o[2 * i][0]; f[i].w[1] = o[2 * i][1];
     f[i].w[2] = o[2 * i + 1][0]; f[i].w[3] = o[2 * i + 1][1];
+  }
+}
+
+
+// ----------------------------------------------------------------- loop-invariant LDS offsets
+//
+// Within a row-major swizzled tile, the swizzle of a row depends on the row
+// modulo 16 only, and every 16-row slice a lane reads sits at the same row
+// modulo 16.  So the swizzled byte offset of everything a lane reads from a
+// tile is a per-lane constant plus a multiple of 16 rows, which becomes an
+// instruction immediate.
+
+// Per-lane byte offsets of the transposed (ds_read_b64_tr_b16) reads of a bf16
+// tile: o[cb] addresses column block cb (columns 16cb..16cb+15) of rows
+// 4g + (l16 >> 2) (+ 16-row multiples added as immediates).
+template <int D>
+struct TrOffsets {
+  uint32_t o[D / 16];
+  __device__ __forceinline__ void init() {
+    using RT = RowTile<uint16_t, D>;
+    const int l = lane_id(), j = l & 15, g = l >> 4;
+    const int r = 4 * g + (j >> 2);
+    const int u0 = (j & 3) >> 1, half = j & 1;
+    const uint32_t low = (uint32_t)(((u0 ^ RT::swz(r)) << 4) | (half << 3));
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb)
+      o[cb] = (uint32_t)(r * RT::kUnits * 16) + (low ^ (uint32_t)(32 * cb));
+  }
+};
+
+// Eight transposed reads at a[i] + I_i, waited for inside the block (see
+// tr_read8).  Fragment i takes items 0..3 from read 2i and 4..7 from 2i+1.
+template <int I0, int I1, int I2, int I3, int I4, int I5, int I6, int I7>
+__device__ __forceinline__ void tr_read8_imm(Frag<uint16_t> (&f)[4], const uint32_t (&a)[8]) {
+  u32x2 o[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%17\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%18\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:%19\n\t"
+      "ds_read_b64_tr_b16 %4, %12 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %5, %13 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %6, %14 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:%23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "n"(I0), "n"(I1), "n"(I2), "n"(I3), "n"(I4), "n"(I5), "n"(I6), "n"(I7)
+      : "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i].w[0] = o[2 * i][0]; f[i].w[1] = o[2 * i][1];
+    f[i].w[2] = o[2 * i + 1][0]; f[i].w[3] = o[2 * i + 1][1];
+  }
+}
+
+
+// The same eight reads through the compiler builtin: the compiler schedules
+// them and waits only for the results it needs (lgkmcnt), so the reads
+// overlap MFMAs.  Valid because the direct LDS loads are issued from inline
+// asm that the compiler does not track (it would otherwise guard every LDS
+// read with a full vmcnt wait).
+template <int I0, int I1, int I2, int I3, int I4, int I5, int I6, int I7>
+__device__ __forceinline__ void tr_read8_sched(Frag<uint16_t> (&f)[4], const uint32_t (&a)[8]) {
+  constexpr int imm[8] = {I0, I1, I2, I3, I4, I5, I6, I7};
+  v4i16 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    o[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(a[i] + imm[i]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v4i16 x = o[2 * i], y = o[2 * i + 1];
+    f[i].w[0] = (uint32_t)(uint16_t)x[0] | ((uint32_t)(uint16_t)x[1] << 16);
+    f[i].w[1] = (uint32_t)(uint16_t)x[2] | ((uint32_t)(uint16_t)x[3] << 16);
+    f[i].w[2] = (uint32_t)(uint16_t)y[0] | ((uint32_t)(uint16_t)y[1] << 16);
+    f[i].w[3] = (uint32_t)(uint16_t)y[2] | ((uint32_t)(uint16_t)y[3] << 16);
+  }
+}
+
+// Per-lane byte offsets of the row-operand (ds_read_b128) reads of a tile:
+// o[s] addresses row l16 (+ 16-row multiples as immediates), elements
+// 32s + 8g .. 32s + 8g + 7 (bf16: one unit; fp32: two units, the second at
+// o[s] ^ 16).
+template <typename T, int D>
+struct RowOffsets {
+  uint32_t o[D / 32];
+  __device__ __forceinline__ void init() {
+    using RT = RowTile<T, D>;
+    const int l = lane_id(), j = l & 15, g = l >> 4;
+    constexpr int upf = Elem<T>::kBytes / 2;   // units per 8 elements
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+      o[s] = (uint32_t)(j * RT::kUnits * 16) + (uint32_t)((((4 * s + g) * upf) ^ RT::swz(j)) << 4);
+  }
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void frag_rows_at(Frag<T>& f, const char* p) {
+  if constexpr (Elem<T>::kBytes == 2) {
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    f.w[0] = x.x; f.w[1] = x.y; f.w[2] = x.z; f.w[3] = x.w;
+  } else {
+    // the swizzled units of logical units 2u and 2u+1 differ in their lowest bit,
+    // i.e. in bit 4 of the (32-byte aligned) LDS byte address
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    const float4 y = *reinterpret_cast<const float4*>(reinterpret_cast<uintptr_t>(p) ^ 16u);
+    f.v[0] = x.x; f.v[1] = x.y; f.v[2] = x.z; f.v[3] = x.w;
+    f.v[4] = y.x; f.v[5] = y.y; f.v[6] = y.z; f.v[7] = y.w;
   }
 }
 

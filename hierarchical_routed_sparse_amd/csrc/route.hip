@@ -7,18 +7,21 @@
 // within a block depends on several query positions, which is why the block
 // is routed as a whole (its routing query is the mean of its 64 queries).
 //
-// One wavefront owns one routing row (b, hq, block); a workgroup holds four
-// rows, ordered so that the query heads of one kv head and one block sit in
-// the same workgroup (they read the same summaries) and the rows of one kv
-// head stay on one XCD.  Per row:
-//   1. block query = mean of the 64 query rows (fp32);
-//   2. lane l scores chunks l, l+64, ... (fp32 dot products, fixed order);
-//   3. top-k by a wave-level radix select on order-preserving 32-bit keys:
-//      32 rounds of ballot/popcount fix the k-th largest key bit by bit; ties
-//      at that key are resolved toward the lower index by a ballot prefix
-//      count, and kept indices are compacted in ascending order the same way;
-//   4. the 8 groups of every kept chunk are scored and the top-g taken jointly
-//      with the same selection.
+// One workgroup per (b, kv head, block, set of up to 4 query heads of that kv
+// head); those rows share the candidate chunks and the summaries.
+//   1. each wavefront computes one row's block query (mean of its 64 query
+//      rows: 16 independent 16-byte loads per lane, then a cross-lane sum);
+//   2. chunk scores: lane l of wavefront w scores chunks 256j + 64w + l for
+//      every row of the set, so each chunk summary is loaded once for all rows
+//      (fp32 dot products in a fixed order); scores go to LDS;
+//   3. wavefront r selects row r's top-k by a wave-level radix select on
+//      order-preserving 32-bit keys: 32 rounds of per-lane counting and a
+//      wave-wide sum fix the k-th largest key bit by bit, ties at that key go
+//      to the lower index by a ballot prefix count, and kept indices are
+//      compacted in ascending order the same way;
+//   4. all threads score the 8 groups of every kept chunk of every row (one
+//      candidate per thread at a time, scores to LDS); then wavefront r takes
+//      row r's top-g jointly with the same selection.
 #include "hga_device.h"
 #include "hga_kernels.h"
 
@@ -26,7 +29,7 @@ namespace hga {
 namespace {
 
 constexpr int kMaxTopK = 64;
-constexpr int kGroupSlots = 8;  // up to 512 group candidates per row
+constexpr int kRowsPerWG = 4;
 
 struct RouteP {
   const void* Q;
@@ -34,7 +37,7 @@ struct RouteP {
   const float* gm;
   int32_t* cidx;
   int32_t* gidx;
-  int B, Hq, Hkv, Sq, Skv, q0, nblk, top_k, top_g, nrows;
+  int B, Hq, Hkv, Sq, Skv, q0, nblk, top_k, top_g, nsets, nwork;
 };
 
 // Order-preserving map from finite fp32 to uint32 (larger float -> larger key).
@@ -45,7 +48,10 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 }
 
 // Marks the kk best of the n candidates held as key[j] by lane l for candidate
-// index 64*j + l (best = larger key, then lower index).
+// index 64*j + l (best = larger key, then lower index).  Slots and lanes past
+// the n-th candidate must hold key 0: every real key is >= 0x00800000 (see
+// order_key) and every trial threshold is >= 1, so they are never counted and
+// the loops need no per-slot guards (no divergent branches).
 template <int NS>
 __device__ __forceinline__ void select_best(const uint32_t (&key)[NS], int n, int kk, bool (&sel)[NS]) {
   const int lane = lane_id();
@@ -60,172 +66,246 @@ __device__ __forceinline__ void select_best(const uint32_t (&key)[NS], int n, in
     return;
   }
   // largest threshold T with #{key >= T} >= kk, i.e. the kk-th largest key
+  // (counted per lane in VALU registers, then one wave-wide sum per round: a
+  // ballot per slot would chain every compare through the VCC register)
   uint32_t T = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t trial = T | (1u << bit);
-    int cnt = 0;
+    int c = 0;
 #pragma unroll
-    for (int j = 0; j < NS; ++j)
-      if (64 * j < n) cnt += __popcll(__ballot(64 * j + lane < n && key[j] >= trial));
-    if (cnt >= kk) T = trial;
+    for (int j = 0; j < NS; ++j) c += key[j] >= trial ? 1 : 0;
+    if (wave_sum(c) >= kk) T = trial;
   }
-  int gt = 0;
+  int gl = 0;
 #pragma unroll
-  for (int j = 0; j < NS; ++j)
-    if (64 * j < n) gt += __popcll(__ballot(64 * j + lane < n && key[j] > T));
+  for (int j = 0; j < NS; ++j) gl += key[j] > T ? 1 : 0;
+  const int gt = wave_sum(gl);
   const int need = kk - gt;  // how many of the candidates equal to T are kept
   int eq_before = 0;
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    sel[j] = false;
-    if (64 * j < n) {
-      const bool valid = 64 * j + lane < n;
-      const bool eq = valid && key[j] == T;
-      const uint64_t m = __ballot(eq);
-      const int rank = eq_before + mbcnt(m);
-      sel[j] = valid && (key[j] > T || (eq && rank < need));
-      eq_before += __popcll(m);
-    }
+    const bool eq = key[j] == T;
+    const uint64_t m = __ballot(eq);
+    const int rank = eq_before + mbcnt(m);
+    sel[j] = key[j] > T || (eq && rank < need);
+    eq_before += __popcll(m);
   }
 }
 
+// fp32 dot product of an LDS vector with a global row, element order 0..D-1.
 template <int D>
 __device__ __forceinline__ float dot_row(const float* qbar, const float* row) {
   const float4* r = reinterpret_cast<const float4*>(row);
+  asm volatile("" : "+v"(qbar));   // LDS re-read per call, not hoisted into registers
   const float4* q = reinterpret_cast<const float4*>(qbar);
-  float s = 0.f;
-#pragma unroll 8
+  float4 x[D / 4];
+#pragma unroll
+  for (int i = 0; i < D / 4; ++i) x[i] = r[i];   // all loads in flight at once
+  // four partial sums (elements d = 4i + e, e = 0..3), then (s0 + s1) + (s2 + s3)
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
   for (int i = 0; i < D / 4; ++i) {
-    const float4 a = q[i], b = r[i];
-    s = fmaf(a.x, b.x, s);
-    s = fmaf(a.y, b.y, s);
-    s = fmaf(a.z, b.z, s);
-    s = fmaf(a.w, b.w, s);
+    const float4 a = q[i];
+    s0 = fmaf(a.x, x[i].x, s0);
+    s1 = fmaf(a.y, x[i].y, s1);
+    s2 = fmaf(a.z, x[i].z, s2);
+    s3 = fmaf(a.w, x[i].w, s3);
   }
-  return s;
+  return (s0 + s1) + (s2 + s3);
 }
 
-template <typename T, int D, int NSC>
+template <typename T, int D, int NSC, int NSG>
 __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
-  __shared__ __attribute__((aligned(16))) float s_qbar[4][D];
-  __shared__ int s_chunk[4][kMaxTopK];
+  constexpr int kGroupSlots = NSG;   // group candidates per row: up to 64 * NSG
+  constexpr int kMaxChunks = 64 * NSC;
+  __shared__ __attribute__((aligned(16))) float s_qbar[kRowsPerWG][D];
+  __shared__ float s_score[kRowsPerWG][kMaxChunks];
+  __shared__ int s_chunk[kRowsPerWG][kMaxTopK];
+  __shared__ float s_gscore[kRowsPerWG][8 * kMaxTopK];
 
   const int lane = lane_id(), wv = threadIdx.x >> 6;
-  const int rowid = xcd_remap(blockIdx.x, gridDim.x) * 4 + wv;
-  const bool live = rowid < p.nrows;
-  // row order: (b, hkv, block, query head within the kv group)
+  // work: (b, hkv, block, set of query heads); sets of one kv head run on one XCD
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int r = p.Hq / p.Hkv;
-  int t = live ? rowid : 0;
-  const int hql = t % r;
-  t /= r;
+  int t = w;
+  const int set = t % p.nsets;
+  t /= p.nsets;
   const int blk = t % p.nblk;
   t /= p.nblk;
   const int hkv = t % p.Hkv, b = t / p.Hkv;
-  const int hq = hkv * r + hql;
-  const int cb = p.q0 / kChunk + blk;                 // the block's own chunk
-  const long long orow = ((long long)b * p.Hq + hq) * p.nblk + blk;
+  const int h0 = set * kRowsPerWG;                       // first query head of the set (within the group)
+  const int nrows = min(kRowsPerWG, r - h0);             // rows of this set
+  const int cb = p.q0 / kChunk + blk;                    // the block's own chunk = number of candidates
   const long long nch = p.Skv / kChunk;
 
-  // 1. block query
-  if (live) {
-    constexpr int E = D / 64;
-    const T* Qb = reinterpret_cast<const T*>(p.Q) + (((long long)b * p.Hq + hq) * p.Sq + (long long)blk * kChunk) * D + lane * E;
-    float acc[E];
+  // 1. block query of row wv (head hkv*r + h0 + wv): lane (o = l%16, rg = l/16)
+  //    sums rows 16rg..16rg+15 of columns 8o..8o+7
+  if (wv < nrows) {
+    const int hq = hkv * r + h0 + wv;
+    const T* Qb = reinterpret_cast<const T*>(p.Q) + (((long long)b * p.Hq + hq) * p.Sq + (long long)blk * kChunk) * D;
+    constexpr int kOct = D / 8;                 // 8-element columns
+    constexpr int kRowSets = 64 / kOct;         // lanes along the rows
+    constexpr int kRowsPerLane = kChunk / kRowSets;
+    const int o = lane % kOct, rg = lane / kOct;
+    float acc[8];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    for (int i = 0; i < kChunk; ++i)
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    Frag<T> x[kRowsPerLane];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += to_f32(Qb[(long long)i * D + e]);
+    for (int i = 0; i < kRowsPerLane; ++i) load_frag(x[i], Qb + (long long)(rg * kRowsPerLane + i) * D + 8 * o);
 #pragma unroll
-    for (int e = 0; e < E; ++e) s_qbar[wv][lane * E + e] = acc[e] * (1.0f / 64.0f);
+    for (int i = 0; i < kRowsPerLane; ++i) {
+      const T* v = reinterpret_cast<const T*>(&x[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += to_f32(v[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[e];
+      for (int m = kOct; m < 64; m <<= 1) v += __shfl_xor(v, m);
+      acc[e] = v;
+    }
+    if (rg == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_qbar[wv][8 * o + e] = acc[e] * (1.0f / 64.0f);
+    }
   }
   __syncthreads();
-  const float* qbar = s_qbar[wv];
 
-  // 2-3. chunk scores over the cb chunks before the own chunk, top-k
-  const int nc = live ? cb : 0;
-  const int kk = nc < p.top_k ? nc : p.top_k;
-  if (live) {
+  // 2. chunk scores for every row of the set; each chunk summary loaded once
+  //    (all of its loads in flight together, then the dot products)
+  {
     const float* cmb = p.cm + ((long long)b * p.Hkv + hkv) * nch * D;
+    for (int c = 64 * wv + lane; c < cb; c += kThreads) {
+      const float4* kr = reinterpret_cast<const float4*>(cmb + (long long)c * D);
+      float4 x[D / 4];
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) x[i] = kr[i];
+      // re-read the block queries from LDS every chunk (keeps them out of registers)
+      const float* qall = &s_qbar[0][0];
+      asm volatile("" : "+v"(qall));
+#pragma unroll
+      for (int q = 0; q < kRowsPerWG; ++q) {
+        const float4* qb = reinterpret_cast<const float4*>(qall + q * D);
+        float sc = 0.f;
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) {
+          const float4 a = qb[i];
+          sc = fmaf(a.x, x[i].x, sc);
+          sc = fmaf(a.y, x[i].y, sc);
+          sc = fmaf(a.z, x[i].z, sc);
+          sc = fmaf(a.w, x[i].w, sc);
+        }
+        s_score[q][c] = sc;
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one chunk's loads at a time
+    }
+  }
+  __syncthreads();
+
+  const int nc = cb;
+  const int kk = nc < p.top_k ? nc : p.top_k;    // chunks kept (same for every row)
+  const int ng = 8 * kk;                          // group candidates per row
+  const int gg = ng < p.top_g ? ng : p.top_g;     // groups kept
+
+  // 3. top-k chunks of row wv
+  if (wv < nrows) {
+    const long long orow = ((long long)b * p.Hq + hkv * r + h0 + wv) * p.nblk + blk;
     uint32_t key[NSC];
 #pragma unroll
     for (int j = 0; j < NSC; ++j) {
-      key[j] = 0;
       const int c = 64 * j + lane;
-      if (64 * j < nc && c < nc) key[j] = order_key(dot_row<D>(qbar, cmb + (long long)c * D));
+      key[j] = c < nc ? order_key(s_score[wv][c]) : 0u;
     }
     bool sel[NSC];
     select_best<NSC>(key, nc, kk, sel);
     int base = 0;
 #pragma unroll
     for (int j = 0; j < NSC; ++j) {
-      if (64 * j < nc) {
-        const uint64_t m = __ballot(sel[j]);
-        if (sel[j]) {
-          const int pos = base + mbcnt(m);
-          s_chunk[wv][pos] = 64 * j + lane;
-          if (p.cidx) p.cidx[orow * p.top_k + pos] = 64 * j + lane;
-        }
-        base += __popcll(m);
+      const uint64_t m = __ballot(sel[j]);
+      if (sel[j]) {
+        const int pos = base + mbcnt(m);
+        s_chunk[wv][pos] = 64 * j + lane;
+        if (p.cidx) p.cidx[orow * p.top_k + pos] = 64 * j + lane;
       }
+      base += __popcll(m);
     }
     if (p.cidx)
       for (int i = kk + lane; i < p.top_k; i += 64) p.cidx[orow * p.top_k + i] = -1;
   }
+  if (!p.gidx) return;
   __syncthreads();
 
-  // 4. group scores over the 8 groups of every kept chunk, joint top-g
-  if (live && p.gidx) {
-    const int ng = 8 * kk;
-    const int gg = ng < p.top_g ? ng : p.top_g;
+  // 4a. group scores of every row of the set: all threads share the candidates
+  //     (row q, candidate i = 8 * (rank of the kept chunk) + group in chunk)
+  {
     const float* gmb = p.gm + ((long long)b * p.Hkv + hkv) * nch * 8 * D;
+    for (int u = threadIdx.x; u < nrows * ng; u += kThreads) {
+      const int q = u / ng, i = u % ng;
+      const int gmm = s_chunk[q][i >> 3] * 8 + (i & 7);
+      s_gscore[q][i] = dot_row<D>(s_qbar[q], gmb + (long long)gmm * D);
+      __builtin_amdgcn_sched_barrier(0);   // one candidate's loads at a time
+    }
+  }
+  __syncthreads();
+  if (wv >= nrows) return;   // no barrier below
+
+  // 4b. joint top-g of row wv over its 8 * kk group candidates
+  {
+    const long long orow = ((long long)b * p.Hq + hkv * r + h0 + wv) * p.nblk + blk;
     uint32_t key[kGroupSlots];
-    int gam[kGroupSlots];
 #pragma unroll
     for (int j = 0; j < kGroupSlots; ++j) {
-      key[j] = 0;
-      gam[j] = -1;
       const int i = 64 * j + lane;
-      if (64 * j < ng && i < ng) {
-        gam[j] = s_chunk[wv][i >> 3] * 8 + (i & 7);
-        key[j] = order_key(dot_row<D>(qbar, gmb + (long long)gam[j] * D));
-      }
+      key[j] = i < ng ? order_key(s_gscore[wv][i]) : 0u;
     }
     bool sel[kGroupSlots];
     select_best<kGroupSlots>(key, ng, gg, sel);
     int base = 0;
 #pragma unroll
     for (int j = 0; j < kGroupSlots; ++j) {
-      if (64 * j < ng) {
-        const uint64_t m = __ballot(sel[j]);
-        if (sel[j]) p.gidx[orow * p.top_g + base + mbcnt(m)] = gam[j];
-        base += __popcll(m);
+      const uint64_t m = __ballot(sel[j]);
+      if (sel[j]) {
+        const int i = 64 * j + lane;
+        p.gidx[orow * p.top_g + base + mbcnt(m)] = s_chunk[wv][i >> 3] * 8 + (i & 7);
       }
+      base += __popcll(m);
     }
     for (int i = gg + lane; i < p.top_g; i += 64) p.gidx[orow * p.top_g + i] = -1;
   }
 }
 
-template <typename T, int D, int NSC>
+template <typename T, int D, int NSC, int NSG>
 hipError_t run(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
                int32_t* gi, hipStream_t s) {
   RouteP p;
   p.Q = Q; p.cm = cm; p.gm = gm; p.cidx = ci; p.gidx = gi;
   p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.q0 = d.q0;
   p.nblk = d.nblk; p.top_k = d.top_k; p.top_g = d.top_g;
-  p.nrows = d.B * d.Hq * d.nblk;
-  const int nwg = (p.nrows + 3) / 4;
-  route_kernel<T, D, NSC><<<nwg, kThreads, 0, s>>>(p);
+  const int r = d.Hq / d.Hkv;
+  p.nsets = (r + kRowsPerWG - 1) / kRowsPerWG;
+  p.nwork = d.B * d.Hkv * d.nblk * p.nsets;
+  route_kernel<T, D, NSC, NSG><<<p.nwork, kThreads, 0, s>>>(p);
   return hipGetLastError();
+}
+
+template <typename T, int D, int NSC>
+hipError_t run_g(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
+                 int32_t* gi, hipStream_t s) {
+  // 8 * top_k group candidates per row at most
+  if (d.top_k <= 8) return run<T, D, NSC, 1>(d, Q, cm, gm, ci, gi, s);
+  if (d.top_k <= 16) return run<T, D, NSC, 2>(d, Q, cm, gm, ci, gi, s);
+  if (d.top_k <= 32) return run<T, D, NSC, 4>(d, Q, cm, gm, ci, gi, s);
+  return run<T, D, NSC, 8>(d, Q, cm, gm, ci, gi, s);
 }
 
 template <typename T, int D>
 hipError_t run_d(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
                  int32_t* gi, hipStream_t s) {
   const int max_cand = d.Skv / kChunk - 1;   // chunks before the last block's own chunk
-  if (max_cand <= 256) return run<T, D, 4>(d, Q, cm, gm, ci, gi, s);
-  if (max_cand <= 1024) return run<T, D, 16>(d, Q, cm, gm, ci, gi, s);
-  return run<T, D, 32>(d, Q, cm, gm, ci, gi, s);
+  if (max_cand <= 256) return run_g<T, D, 4>(d, Q, cm, gm, ci, gi, s);
+  if (max_cand <= 1024) return run_g<T, D, 16>(d, Q, cm, gm, ci, gi, s);
+  return run_g<T, D, 32>(d, Q, cm, gm, ci, gi, s);
 }
 
 }  // namespace
