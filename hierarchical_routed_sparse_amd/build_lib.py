@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libhga.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["hga_api.hip", "summaries.hip", "route.hip", "attend_fwd.hip", "attend_bwd.hip"]
-HEADERS = ["hga_device.h", "hga_kernels.h"]
+HEADERS = ["hga_device.h", "hga_kernels.h", "bwd_common.h"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -13,15 +13,18 @@
 //  * bwd_dq  -- one workgroup per (b, hq, block): the forward's tile walk (own
 //    chunk, then the kept groups), K and V tiles gathered into LDS with direct
 //    loads; writes delta and dQ.  dQ^T += K^T . dS^T reads K^T with the LDS
-//    transpose read.
-//  * bwd_dkdv -- one workgroup per (b, hkv, chunk of 64 keys).  It finds, for
-//    every (query head of the kv group, query block), which of the chunk's 8
-//    groups that row kept (binary search in the ascending routing row) or
-//    whether the chunk is the row's own chunk (causal), compacts those rows in
-//    a fixed order, and walks them with the rows' Q and dO tiles gathered into
-//    LDS by direct loads; wavefront w owns keys 16w..16w+15 and skips rows that
-//    kept neither of its two groups.  Each key's dK/dV is summed by one
-//    wavefront in that fixed order: no atomics, bitwise reproducible.
+//    transpose read.  It also writes the row's entry of the group-mask map
+//    (byte c = which of chunk c's 8 groups the row kept) for the dK/dV pass.
+//  * bwd_dkdv -- one workgroup per (b, hkv, chunk of 64 keys).  It
+//    lists, in a fixed order, every (query head of the kv group, query block)
+//    whose mask for the chunk is non-zero or whose own chunk it is (causal),
+//    and walks them with the rows' Q and dO tiles gathered into LDS by direct
+//    loads; wavefront w owns keys 16w..16w+15 and skips rows that kept neither
+//    of its two groups.  Each key's dK/dV is summed by one wavefront in that
+//    fixed order: no atomics, bitwise reproducible.
+#include <type_traits>
+
+#include "bwd_common.h"
 #include "hga_device.h"
 #include "hga_kernels.h"
 
@@ -39,7 +42,6 @@ namespace hga {
 namespace {
 
 constexpr int kMaxTopG = 512;
-constexpr int kRowsPerPass = 1024;   // routing rows examined per entry-list build
 
 // Compacts the routing row (groups in [0, 8*cb), order kept) into s_glist and
 // returns how many were kept.  Every thread of the workgroup must call it.
@@ -79,6 +81,7 @@ struct DqP {
   const int32_t* gidx;
   void* dQ;
   float* delta;
+  uint8_t* cmask;   // [routing row][chunk] kept-group masks, for the dK/dV kernel
   int B, Hq, Hkv, Sq, Skv, q0, nblk, top_g, nwork;
   float scale;
 };
@@ -284,6 +287,28 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dq_kernel(const DqP p) {
 
   // stores only after the tile pipeline: its vmcnt waits count direct loads only
   if (g4 == 0) p.delta[qrow0 + qq] = delta;
+
+  // the row of the group-mask map: byte c = mask of the kept groups of chunk c
+  // (built in LDS, the stage buffers being free once every wave is past them)
+  {
+    __syncthreads();
+    const int nch = p.Skv / kChunk;
+    uint8_t* s_cm = reinterpret_cast<uint8_t*>(smem);
+    for (int i = tid; i < nch; i += kThreads) s_cm[i] = 0;
+    __syncthreads();
+    // the last kept group of each chunk (the list is ascending) ORs the run
+    for (int i = tid; i < nvalid; i += kThreads) {
+      const int ch = s_glist[i] >> 3;
+      if (i + 1 == nvalid || (s_glist[i + 1] >> 3) != ch) {
+        uint32_t m = 0;
+        for (int j = i; j >= 0 && (s_glist[j] >> 3) == ch; --j) m |= 1u << (s_glist[j] & 7);
+        s_cm[ch] = (uint8_t)m;
+      }
+    }
+    __syncthreads();
+    uint8_t* out = p.cmask + (long long)row * nch;
+    for (int i = tid; i < nch; i += kThreads) out[i] = s_cm[i];
+  }
   T* dq = reinterpret_cast<T*>(p.dQ) + (qrow0 + qq) * D + 4 * g4;
   const float sc = p.scale;
 #pragma unroll
@@ -292,55 +317,6 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dq_kernel(const DqP p) {
 }
 
 // ============================================================== dK, dV
-
-struct DkvP {
-  const void* Q;
-  const void* K;
-  const void* V;
-  const float* lse;
-  const void* dO;
-  const int32_t* gidx;
-  const float* delta;
-  void* dK;
-  void* dV;
-  int B, Hq, Hkv, Sq, Skv, q0, nblk, top_g, nchunks, nwork;
-  float scale;
-};
-
-// entry word: (row << 9) | mask, mask bits 0..7 = kept groups, bit 8 = own chunk
-constexpr uint32_t kLocalBit = 1u << 8;
-
-// Group mask of chunk c in one ascending, -1 padded routing row g[0..top_g):
-// bit t set when group 8c+t is kept.  Two rounds of independent loads: 16
-// evenly spaced samples bracket the position of the first group >= 8c, then
-// the bracket plus the 8 slots after it are read.
-__device__ __forceinline__ uint32_t chunk_mask(const int32_t* g, int top_g, int c) {
-  const int lo_g = 8 * c;
-  const int stride = (top_g + 15) >> 4;
-  int below = 0;   // samples holding a valid group below chunk c
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int idx = i * stride;
-    const int v = idx < top_g ? g[idx] : -1;
-    below += (v >= 0 && v < lo_g) ? 1 : 0;
-  }
-  // every entry before sample `below - 1` is below chunk c; chunk c's groups
-  // (at most 8) start in [lo, lo + stride]
-  const int lo = below > 0 ? (below - 1) * stride : 0;
-  uint32_t mask = 0;
-  for (int i0 = 0; i0 < stride + 8; i0 += 16) {
-    int v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int idx = lo + i0 + i;
-      v[i] = (i0 + i < stride + 8 && idx < top_g) ? g[idx] : -1;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (v[i] >= lo_g && v[i] < lo_g + 8) mask |= 1u << (v[i] - lo_g);
-  }
-  return mask;
-}
 
 template <typename T, int D, int S>
 __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p) {
@@ -386,13 +362,17 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
     dvacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float c2 = p.scale * kLog2e;
-  const int blk_first = c - p.q0 / kChunk;   // rows with block >= this can touch chunk c
 
   // loop-invariant per-lane offsets (see attend_fwd.hip)
-  RowOffsets<T, D> qro;
+  // bf16: query rows in perm_row order (conflict-free transposing reads);
+  // fp32: natural order
+  using QRO = std::conditional_t<sizeof(T) == 2, RowOffsetsPerm<D>, RowOffsets<T, D>>;
+  QRO qro;
   qro.init();
-  TrOffsets<(sizeof(T) == 2 ? D : 16)> qto;
+  TrOffsetsPerm<(sizeof(T) == 2 ? D : 16)> qto;
   if constexpr (sizeof(T) == 2) qto.init();
+  // query (within its 16-row slice) of result item i of this lane's group
+  auto qperm = [&](int i) { return sizeof(T) == 2 ? 4 * i + perm_sigma(g4) : 4 * g4 + i; };
   uint32_t ld_off[kIssues];
 #pragma unroll
   for (int j = 0; j < kIssues; ++j) {
@@ -424,34 +404,7 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
 
   for (int r0 = 0; r0 < nrows; r0 += kRowsPerPass) {
     // ---- entry list for routing rows [r0, r0 + kRowsPerPass)
-    int nent = 0;
-    for (int base = 0; base < kRowsPerPass && r0 + base < nrows; base += kThreads) {
-      const int rr = r0 + base + tid;
-      uint32_t mask = 0;
-      if (rr < nrows) {
-        const int hq = hkv * r + rr / p.nblk, blk = rr % p.nblk;
-        if (blk == blk_first) {
-          mask = kLocalBit | 0xFFu;
-        } else if (blk > blk_first) {
-          mask = chunk_mask(p.gidx + (((long long)b * p.Hq + hq) * p.nblk + blk) * p.top_g,
-                            p.top_g, c);
-        }
-      }
-      const bool f = mask != 0;
-      const uint64_t bal = __ballot(f);
-      if (lane == 0) s_wsum[wv] = __popcll(bal);
-      __syncthreads();
-      int off = 0, tot = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = s_wsum[i];
-        off += i < wv ? v : 0;
-        tot += v;
-      }
-      if (f) s_ent[nent + off + mbcnt(bal)] = ((uint32_t)rr << 9) | mask;
-      nent += tot;
-      __syncthreads();
-    }
+    const int nent = build_entries(p, b, hkv, c, r0, s_ent, s_wsum);
     if (nent == 0) continue;
 
     // ---- walk the entries, S - 1 of them in flight
@@ -496,15 +449,17 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
 #pragma unroll
         for (int qs = 0; qs < 4; ++qs) {
           // queries 16qs + 4g + i: stats of wave-slot qs at [lse 16 | delta 16]
-          const float4 l4 = reinterpret_cast<const float4*>(stat + 32 * qs)[g4];
-          const float4 d4 = reinterpret_cast<const float4*>(stat + 32 * qs + 16)[g4];
-          const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dq[4] = {d4.x, d4.y, d4.z, d4.w};
+          float lq[4], dq[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            lq[i] = stat[32 * qs + qperm(i)];
+            dq[i] = stat[32 * qs + 16 + qperm(i)];
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float nl = kvalid ? -lq[i] * kLog2e : -INFINITY;
             float pr = __builtin_amdgcn_exp2f(fmaf(sacc[qs][i], c2, nl));
-            if (local && kin > 16 * qs + 4 * g4 + i) pr = 0.f;
+            if (local && kin > 16 * qs + qperm(i)) pr = 0.f;
             sacc[qs][i] = pr;
             dpacc[qs][i] = pr * (dpacc[qs][i] - dq[i]);
           }
@@ -515,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
         frag_from_acc(dsf[0], dpacc[0], dpacc[1]);
         frag_from_acc(dsf[1], dpacc[2], dpacc[3]);
         // dV^T += dO^T . P and dK^T += Q^T . dS; the transposed operands cover
-        // queries 32mm+4g+t, 32mm+16+4g+t of column block cb
+        // queries 32mm + qperm(t), 32mm + 16 + qperm(t) of column block cb
         if constexpr (sizeof(T) == 2) {
           uint32_t qa[D / 16];
 #pragma unroll
@@ -570,10 +525,10 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
 template <typename T, int D>
 hipError_t run_dq(const Dims& d, const void* Q, const void* K, const void* V, const void* O,
                   const float* lse, const void* dO, const int32_t* gi, void* dQ, float* delta,
-                  hipStream_t s) {
+                  uint8_t* cmask, hipStream_t s) {
   DqP p;
   p.Q = Q; p.K = K; p.V = V; p.O = O; p.lse = lse; p.dO = dO; p.gidx = gi; p.dQ = dQ;
-  p.delta = delta;
+  p.delta = delta; p.cmask = cmask;
   p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.q0 = d.q0;
   p.nblk = d.nblk; p.top_g = d.top_g; p.scale = d.scale;
   p.nwork = d.B * d.Hq * d.nblk;
@@ -588,10 +543,11 @@ hipError_t run_dq(const Dims& d, const void* Q, const void* K, const void* V, co
 
 template <typename T, int D>
 hipError_t run_dkdv(const Dims& d, const void* Q, const void* K, const void* V, const float* lse,
-                    const void* dO, const int32_t* gi, const float* delta, void* dK, void* dV,
-                    hipStream_t s) {
+                    const void* dO, const int32_t* gi, const float* delta, const uint8_t* cmask,
+                    void* dK, void* dV, hipStream_t s) {
   DkvP p;
   p.Q = Q; p.K = K; p.V = V; p.lse = lse; p.dO = dO; p.gidx = gi; p.delta = delta;
+  p.cmask = cmask;
   p.dK = dK; p.dV = dV;
   p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.q0 = d.q0;
   p.nblk = d.nblk; p.top_g = d.top_g; p.scale = d.scale;
@@ -610,22 +566,23 @@ hipError_t run_dkdv(const Dims& d, const void* Q, const void* K, const void* V, 
 hipError_t launch_attend_bwd_dq(const Dims& d, const void* Q, const void* K, const void* V,
                                 const void* O, const float* lse, const void* dO,
                                 const int32_t* group_idx, void* dQ, float* delta,
-                                hipStream_t s) {
+                                uint8_t* cmask, hipStream_t s) {
   if (d.bf16)
-    return d.D == 128 ? run_dq<uint16_t, 128>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, s)
-                      : run_dq<uint16_t, 64>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, s);
-  return d.D == 128 ? run_dq<float, 128>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, s)
-                    : run_dq<float, 64>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, s);
+    return d.D == 128 ? run_dq<uint16_t, 128>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, s)
+                      : run_dq<uint16_t, 64>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, s);
+  return d.D == 128 ? run_dq<float, 128>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, s)
+                    : run_dq<float, 64>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, s);
 }
 
 hipError_t launch_attend_bwd_dkdv(const Dims& d, const void* Q, const void* K, const void* V,
                                   const float* lse, const void* dO, const int32_t* group_idx,
-                                  const float* delta, void* dK, void* dV, hipStream_t s) {
+                                  const float* delta, const uint8_t* cmask, void* dK, void* dV,
+                                  hipStream_t s) {
   if (d.bf16)
-    return d.D == 128 ? run_dkdv<uint16_t, 128>(d, Q, K, V, lse, dO, group_idx, delta, dK, dV, s)
-                      : run_dkdv<uint16_t, 64>(d, Q, K, V, lse, dO, group_idx, delta, dK, dV, s);
-  return d.D == 128 ? run_dkdv<float, 128>(d, Q, K, V, lse, dO, group_idx, delta, dK, dV, s)
-                    : run_dkdv<float, 64>(d, Q, K, V, lse, dO, group_idx, delta, dK, dV, s);
+    return d.D == 128 ? run_dkdv<uint16_t, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, s)
+                      : run_dkdv<uint16_t, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, s);
+  return d.D == 128 ? run_dkdv<float, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, s)
+                    : run_dkdv<float, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, s);
 }
 
 }  // namespace hga

@@ -1,0 +1,71 @@
+// Shared by the two dK/dV kernels: their parameters and the inverse routing
+// map (which routing rows attend a given 64-key chunk, and with which groups).
+#pragma once
+#include "hga_device.h"
+
+namespace hga {
+
+struct DkvP {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* lse;
+  const void* dO;
+  const int32_t* gidx;
+  const float* delta;
+  const uint8_t* cmask;   // [routing row][chunk] kept-group masks (from the dQ kernel)
+  void* dK;
+  void* dV;
+  int B, Hq, Hkv, Sq, Skv, q0, nblk, top_g, nchunks, nwork;
+  float scale;
+};
+
+constexpr int kRowsPerPass = 1024;   // routing rows examined per entry-list build
+
+// entry word: (row << 9) | mask, mask bits 0..7 = kept groups, bit 8 = own chunk
+constexpr uint32_t kLocalBit = 1u << 8;
+
+// Entry list of chunk c over routing rows [r0, r0 + kRowsPerPass): every
+// (query head of kv head hkv, block) row that kept a group of chunk c, or
+// whose own chunk is c, in ascending row order (head-major); only rows whose
+// mask meets `want` (groups of interest | kLocalBit) are listed.  Returns the
+// count.  Every thread of the (256-thread) workgroup must call it; s_ent is
+// valid for all of them on return.
+__device__ __forceinline__ int build_entries(const DkvP& p, int b, int hkv, int c, int r0,
+                                             uint32_t* s_ent, int* s_wsum,
+                                             uint32_t want = 0x1FFu) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = p.Hq / p.Hkv;
+  const int nrows = r * p.nblk;
+  const int blk_first = c - p.q0 / kChunk;   // rows with block >= this can touch chunk c
+  int nent = 0;
+  for (int base = 0; base < kRowsPerPass && r0 + base < nrows; base += kThreads) {
+    const int rr = r0 + base + tid;
+    uint32_t mask = 0;
+    if (rr < nrows) {
+      const int hq = hkv * r + rr / p.nblk, blk = rr % p.nblk;
+      if (blk == blk_first) {
+        mask = kLocalBit | 0xFFu;
+      } else if (blk > blk_first) {
+        mask = p.cmask[(((long long)b * p.Hq + hq) * p.nblk + blk) * p.nchunks + c];
+      }
+    }
+    const bool f = (mask & want) != 0;
+    const uint64_t bal = __ballot(f);
+    if (lane == 0) s_wsum[wv] = __popcll(bal);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = s_wsum[i];
+      off += i < wv ? v : 0;
+      tot += v;
+    }
+    if (f) s_ent[nent + off + mbcnt(bal)] = ((uint32_t)rr << 9) | mask;
+    nent += tot;
+    __syncthreads();
+  }
+  return nent;
+}
+
+}  // namespace hga

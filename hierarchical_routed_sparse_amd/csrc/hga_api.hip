@@ -28,10 +28,18 @@ hga::Dims dims_of(const hga_shape* s) {
 
 hga_status from_hip(hipError_t e) { return e == hipSuccess ? HGA_OK : HGA_ERR_HIP; }
 
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// workspace: delta (fp32 per query row), then the group-mask map (one byte per
+// (routing row, chunk))
 size_t delta_bytes(const hga_shape* s) {
-  const size_t n = (size_t)s->batch * s->n_q_heads * s->q_len * sizeof(float);
-  return (n + 255) & ~(size_t)255;
+  return round256((size_t)s->batch * s->n_q_heads * s->q_len * sizeof(float));
 }
+size_t cmask_bytes(const hga_shape* s) {
+  return round256((size_t)s->batch * s->n_q_heads * (s->q_len / HGA_QBLOCK) *
+                  (s->kv_len / HGA_CHUNK));
+}
+size_t workspace_bytes(const hga_shape* s) { return delta_bytes(s) + cmask_bytes(s); }
 
 }  // namespace
 
@@ -118,7 +126,7 @@ hga_status hga_attend_bwd_workspace(const hga_shape* shape, size_t* bytes) {
   hga_status st = hga_validate_shape(shape);
   if (st != HGA_OK) return st;
   if (!bytes) return HGA_ERR_NULL;
-  *bytes = delta_bytes(shape);
+  *bytes = workspace_bytes(shape);
   return HGA_OK;
 }
 
@@ -130,9 +138,10 @@ hga_status hga_attend_bwd_dq(const hga_shape* shape, const void* Q, const void* 
   if (st != HGA_OK) return st;
   if (!Q || !K || !V || !O || !lse || !dO || !dQ) return HGA_ERR_NULL;
   if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
-  if (!workspace || workspace_bytes < delta_bytes(shape)) return HGA_ERR_WORKSPACE;
-  return from_hip(hga::launch_attend_bwd_dq(dims_of(shape), Q, K, V, O, lse, dO, group_idx, dQ,
-                                            (float*)workspace, (hipStream_t)stream));
+  if (!workspace || workspace_bytes < ::workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
+  return from_hip(hga::launch_attend_bwd_dq(
+      dims_of(shape), Q, K, V, O, lse, dO, group_idx, dQ, (float*)workspace,
+      (uint8_t*)workspace + delta_bytes(shape), (hipStream_t)stream));
 }
 
 hga_status hga_attend_bwd_dkdv(const hga_shape* shape, const void* Q, const void* K,
@@ -143,10 +152,10 @@ hga_status hga_attend_bwd_dkdv(const hga_shape* shape, const void* Q, const void
   if (st != HGA_OK) return st;
   if (!Q || !K || !V || !lse || !dO || !dK || !dV) return HGA_ERR_NULL;
   if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
-  if (!workspace || workspace_bytes < delta_bytes(shape)) return HGA_ERR_WORKSPACE;
-  return from_hip(hga::launch_attend_bwd_dkdv(dims_of(shape), Q, K, V, lse, dO, group_idx,
-                                              (const float*)workspace, dK, dV,
-                                              (hipStream_t)stream));
+  if (!workspace || workspace_bytes < ::workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
+  return from_hip(hga::launch_attend_bwd_dkdv(
+      dims_of(shape), Q, K, V, lse, dO, group_idx, (const float*)workspace,
+      (const uint8_t*)workspace + delta_bytes(shape), dK, dV, (hipStream_t)stream));
 }
 
 hga_status hga_attend_bwd(const hga_shape* shape, const void* Q, const void* K, const void* V,
@@ -157,7 +166,7 @@ hga_status hga_attend_bwd(const hga_shape* shape, const void* Q, const void* K, 
   if (st != HGA_OK) return st;
   if (!Q || !K || !V || !O || !lse || !dO || !dQ || !dK || !dV) return HGA_ERR_NULL;
   if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
-  if (!workspace || workspace_bytes < delta_bytes(shape)) return HGA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < ::workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
   st = hga_attend_bwd_dq(shape, Q, K, V, O, lse, dO, group_idx, dQ, workspace, workspace_bytes,
                          stream);
   if (st != HGA_OK) return st;

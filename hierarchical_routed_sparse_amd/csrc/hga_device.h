@@ -556,6 +556,47 @@ __device__ __forceinline__ void tr_read8_sched(Frag<uint16_t> (&f)[4], const uin
   }
 }
 
+// Row order within a 16-row slice used by the bf16 products whose results
+// feed a transposing read: operand row n holds element perm_row(n) =
+// 4(n % 4) + sigma(n / 4), sigma = (0, 2, 1, 3), so the 16x16 result item i of
+// lane group g is element 4i + sigma(g).  The transposing read that gathers
+// items 0..3 of lane group g then covers rows 4e + sigma(g), e = 0..3: a
+// half-wave reads 8 rows spaced 2 apart, which the row swizzle (unit XOR row
+// mod 16) spreads over all 64 banks; consecutive rows would collide in pairs.
+__device__ __forceinline__ int perm_sigma(int g) { return ((g & 1) << 1) | (g >> 1); }
+__device__ __forceinline__ int perm_row(int n) { return 4 * (n & 3) + perm_sigma(n >> 2); }
+
+// RowOffsets for bf16 with the rows in perm_row order.
+template <int D>
+struct RowOffsetsPerm {
+  uint32_t o[D / 32];
+  __device__ __forceinline__ void init() {
+    using RT = RowTile<uint16_t, D>;
+    const int l = lane_id(), g = l >> 4;
+    const int row = perm_row(l & 15);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+      o[s] = (uint32_t)(row * RT::kUnits * 16) + (uint32_t)(((4 * s + g) ^ RT::swz(row)) << 4);
+  }
+};
+
+// TrOffsets for results in perm_row order: lane j of group g points at row
+// 4(j / 4) + sigma(g) (columns as in TrOffsets).
+template <int D>
+struct TrOffsetsPerm {
+  uint32_t o[D / 16];
+  __device__ __forceinline__ void init() {
+    using RT = RowTile<uint16_t, D>;
+    const int l = lane_id(), j = l & 15, g = l >> 4;
+    const int r = 4 * (j >> 2) + perm_sigma(g);
+    const int u0 = (j & 3) >> 1, half = j & 1;
+    const uint32_t low = (uint32_t)(((u0 ^ RT::swz(r)) << 4) | (half << 3));
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb)
+      o[cb] = (uint32_t)(r * RT::kUnits * 16) + (low ^ (uint32_t)(32 * cb));
+  }
+};
+
 // Per-lane byte offsets of the row-operand (ds_read_b128) reads of a tile:
 // o[s] addresses row l16 (+ 16-row multiples as immediates), elements
 // 32s + 8g .. 32s + 8g + 7 (bf16: one unit; fp32: two units, the second at

@@ -28,10 +28,11 @@ hipError_t launch_attend_fwd(const Dims& d, const void* Q, const void* K, const 
 hipError_t launch_attend_bwd_dq(const Dims& d, const void* Q, const void* K, const void* V,
                                 const void* O, const float* lse, const void* dO,
                                 const int32_t* group_idx, void* dQ, float* delta,
-                                hipStream_t s);
+                                uint8_t* cmask, hipStream_t s);
 
 hipError_t launch_attend_bwd_dkdv(const Dims& d, const void* Q, const void* K, const void* V,
                                   const float* lse, const void* dO, const int32_t* group_idx,
-                                  const float* delta, void* dK, void* dV, hipStream_t s);
+                                  const float* delta, const uint8_t* cmask, void* dK, void* dV,
+                                  hipStream_t s);
 
 }  // namespace hga
