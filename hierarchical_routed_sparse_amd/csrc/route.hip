@@ -11,17 +11,19 @@
 // head); those rows share the candidate chunks and the summaries.
 //   1. each wavefront computes one row's block query (mean of its 64 query
 //      rows: 16 independent 16-byte loads per lane, then a cross-lane sum);
-//   2. chunk scores: lane l of wavefront w scores chunks 256j + 64w + l for
-//      every row of the set, so each chunk summary is loaded once for all rows
-//      (fp32 dot products in a fixed order); scores go to LDS;
+//   2. chunk scores: eight lanes share one summary row (whole 128-byte lines
+//      per load), each summary is loaded once for all rows of the set, and the
+//      block queries stay in registers (fp32, fixed summation order); scores
+//      go to LDS;
 //   3. wavefront r selects row r's top-k by a wave-level radix select on
 //      order-preserving 32-bit keys: 32 rounds of per-lane counting and a
 //      wave-wide sum fix the k-th largest key bit by bit, ties at that key go
 //      to the lower index by a ballot prefix count, and kept indices are
 //      compacted in ascending order the same way;
-//   4. all threads score the 8 groups of every kept chunk of every row (one
-//      candidate per thread at a time, scores to LDS); then wavefront r takes
-//      row r's top-g jointly with the same selection.
+//   4. the wavefronts score the 8 groups of every kept chunk of every row
+//      (one chunk's 8 consecutive group summaries per wavefront step, scores
+//      to LDS); then wavefront r takes row r's top-g jointly with the same
+//      selection.
 #include "hga_device.h"
 #include "hga_kernels.h"
 
@@ -92,26 +94,28 @@ __device__ __forceinline__ void select_best(const uint32_t (&key)[NS], int n, in
   }
 }
 
-// fp32 dot product of an LDS vector with a global row, element order 0..D-1.
-template <int D>
-__device__ __forceinline__ float dot_row(const float* qbar, const float* row) {
-  const float4* r = reinterpret_cast<const float4*>(row);
-  asm volatile("" : "+v"(qbar));   // LDS re-read per call, not hoisted into registers
-  const float4* q = reinterpret_cast<const float4*>(qbar);
-  float4 x[D / 4];
-#pragma unroll
-  for (int i = 0; i < D / 4; ++i) x[i] = r[i];   // all loads in flight at once
-  // four partial sums (elements d = 4i + e, e = 0..3), then (s0 + s1) + (s2 + s3)
+// Partial dot product of a lane's kV float4s (elements 4(j8 + 8m) + e):
+// four running sums (one per e), added as (s0 + s1) + (s2 + s3).
+template <int kV>
+__device__ __forceinline__ float dot4s(const float4 (&a)[kV], const float4 (&x)[kV]) {
   float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-  for (int i = 0; i < D / 4; ++i) {
-    const float4 a = q[i];
-    s0 = fmaf(a.x, x[i].x, s0);
-    s1 = fmaf(a.y, x[i].y, s1);
-    s2 = fmaf(a.z, x[i].z, s2);
-    s3 = fmaf(a.w, x[i].w, s3);
+  for (int m = 0; m < kV; ++m) {
+    s0 = fmaf(a[m].x, x[m].x, s0);
+    s1 = fmaf(a[m].y, x[m].y, s1);
+    s2 = fmaf(a[m].z, x[m].z, s2);
+    s3 = fmaf(a[m].w, x[m].w, s3);
   }
   return (s0 + s1) + (s2 + s3);
+}
+
+// Sum over the 8 lanes 8k..8k+7 (every lane of the group gets the sum):
+// neighbours, then pairs, then the other half of the group.
+__device__ __forceinline__ float sum8(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  return v;
 }
 
 template <typename T, int D, int NSC, int NSG>
@@ -172,33 +176,34 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
   }
   __syncthreads();
 
-  // 2. chunk scores for every row of the set; each chunk summary loaded once
-  //    (all of its loads in flight together, then the dot products)
+  // 2. chunk scores for every row of the set.  Eight lanes share one summary
+  //    row (lane j8 reads float4s j8, j8 + 8, ..., so each load instruction
+  //    covers whole 128-byte lines), eight rows per wavefront step; the block
+  //    queries stay in registers.  Per row: per-lane partial sums in a fixed
+  //    order, then a fixed 8-lane reduction.
+  constexpr int kV = D / 32;                  // float4s per lane per summary row
+  const int j8 = lane & 7, rsub = lane >> 3;
+  float4 qv[kRowsPerWG][kV];
+#pragma unroll
+  for (int q = 0; q < kRowsPerWG; ++q)
+#pragma unroll
+    for (int m = 0; m < kV; ++m)
+      qv[q][m] = reinterpret_cast<const float4*>(&s_qbar[q][0])[j8 + 8 * m];
   {
     const float* cmb = p.cm + ((long long)b * p.Hkv + hkv) * nch * D;
-    for (int c = 64 * wv + lane; c < cb; c += kThreads) {
-      const float4* kr = reinterpret_cast<const float4*>(cmb + (long long)c * D);
-      float4 x[D / 4];
+    for (int c0 = 8 * wv; c0 < cb; c0 += 32) {
+      const int c = c0 + rsub;
+      const bool live = c < cb;
+      const float4* kr = reinterpret_cast<const float4*>(cmb + (long long)(live ? c : 0) * D);
+      float4 x[kV];
 #pragma unroll
-      for (int i = 0; i < D / 4; ++i) x[i] = kr[i];
-      // re-read the block queries from LDS every chunk (keeps them out of registers)
-      const float* qall = &s_qbar[0][0];
-      asm volatile("" : "+v"(qall));
+      for (int m = 0; m < kV; ++m) x[m] = kr[j8 + 8 * m];
 #pragma unroll
       for (int q = 0; q < kRowsPerWG; ++q) {
-        const float4* qb = reinterpret_cast<const float4*>(qall + q * D);
-        float sc = 0.f;
-#pragma unroll
-        for (int i = 0; i < D / 4; ++i) {
-          const float4 a = qb[i];
-          sc = fmaf(a.x, x[i].x, sc);
-          sc = fmaf(a.y, x[i].y, sc);
-          sc = fmaf(a.z, x[i].z, sc);
-          sc = fmaf(a.w, x[i].w, sc);
-        }
-        s_score[q][c] = sc;
+        if (q >= nrows) break;
+        const float sc = sum8(dot4s<kV>(qv[q], x));
+        if (live && j8 == 0) s_score[q][c] = sc;
       }
-      __builtin_amdgcn_sched_barrier(0);   // one chunk's loads at a time
     }
   }
   __syncthreads();
@@ -236,15 +241,23 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
   if (!p.gidx) return;
   __syncthreads();
 
-  // 4a. group scores of every row of the set: all threads share the candidates
-  //     (row q, candidate i = 8 * (rank of the kept chunk) + group in chunk)
+  // 4a. group scores of every row of the set: one wavefront step covers the
+  //     8 groups of one kept chunk of one row (8 consecutive summary rows);
+  //     candidate i = 8 * (rank of the kept chunk) + group in chunk
   {
     const float* gmb = p.gm + ((long long)b * p.Hkv + hkv) * nch * 8 * D;
-    for (int u = threadIdx.x; u < nrows * ng; u += kThreads) {
-      const int q = u / ng, i = u % ng;
-      const int gmm = s_chunk[q][i >> 3] * 8 + (i & 7);
-      s_gscore[q][i] = dot_row<D>(s_qbar[q], gmb + (long long)gmm * D);
-      __builtin_amdgcn_sched_barrier(0);   // one candidate's loads at a time
+#pragma unroll
+    for (int q = 0; q < kRowsPerWG; ++q) {
+      if (q >= nrows) break;
+      for (int i = wv; i < kk; i += 4) {
+        const int g = s_chunk[q][i] * 8 + rsub;
+        const float4* gr = reinterpret_cast<const float4*>(gmb + (long long)g * D);
+        float4 x[kV];
+#pragma unroll
+        for (int m = 0; m < kV; ++m) x[m] = gr[j8 + 8 * m];
+        const float sc = sum8(dot4s<kV>(qv[q], x));
+        if (j8 == 0) s_gscore[q][8 * i + rsub] = sc;
+      }
     }
   }
   __syncthreads();
