@@ -29,17 +29,19 @@ constexpr uint32_t kLocalBit = 1u << 8;
 // (query head of kv head hkv, block) row that kept a group of chunk c, or
 // whose own chunk is c, in ascending row order (head-major); only rows whose
 // mask meets `want` (groups of interest | kLocalBit) are listed.  Returns the
-// count.  Every thread of the (256-thread) workgroup must call it; s_ent is
-// valid for all of them on return.
+// count.  Every thread of the NT-thread workgroup must call it; s_ent is
+// valid for all of them on return (s_wsum holds NT / 64 ints).
+template <int NT = kThreads>
 __device__ __forceinline__ int build_entries(const DkvP& p, int b, int hkv, int c, int r0,
                                              uint32_t* s_ent, int* s_wsum,
                                              uint32_t want = 0x1FFu) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = p.Hq / p.Hkv;
   const int nrows = r * p.nblk;
   const int blk_first = c - p.q0 / kChunk;   // rows with block >= this can touch chunk c
   int nent = 0;
-  for (int base = 0; base < kRowsPerPass && r0 + base < nrows; base += kThreads) {
+  for (int base = 0; base < kRowsPerPass && r0 + base < nrows; base += NT) {
     const int rr = r0 + base + tid;
     uint32_t mask = 0;
     if (rr < nrows) {
@@ -56,7 +58,7 @@ __device__ __forceinline__ int build_entries(const DkvP& p, int b, int hkv, int 
     __syncthreads();
     int off = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NW; ++i) {
       const int v = s_wsum[i];
       off += i < wv ? v : 0;
       tot += v;
