@@ -86,8 +86,17 @@ struct DqP {
   float scale;
 };
 
+// bf16: the register budget is held to four wavefronts per SIMD (4
+// workgroups per CU, the most the LDS stages allow): the kernel is bound by
+// latency more than by issue, so the extra resident wavefronts pay for the
+// few values the compiler keeps in scratch
+template <typename T>
+constexpr int dq_waves_per_simd() { return sizeof(T) == 2 ? 4 : 2; }
+
 template <typename T, int D, int TK, int S>
-__global__ __launch_bounds__(kThreads) void attend_bwd_dq_kernel(const DqP p) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(dq_waves_per_simd<T>(), dq_waves_per_simd<T>())))
+void attend_bwd_dq_kernel(const DqP p) {
   using RT = RowTile<T, D>;
   constexpr int kTileBytes = TK * RT::kUnits * 16;
   constexpr int kStage = 2 * kTileBytes;                          // K tile | V tile
