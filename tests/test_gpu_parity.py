@@ -141,6 +141,29 @@ def test_outputs_fully_written_and_deterministic():
         assert torch.equal(a, b)
 
 
+def test_split_backward_matches_combined():
+    """hga_attend_bwd_dq then hga_attend_bwd_dkdv (sharing one workspace) give
+    bit for bit what hga_attend_bwd gives."""
+    w = SMALL["bf16_seg_b2"]
+    x = syn.make_inputs(w, with_grad_output=True)
+    t = upload(x, "bf16")
+    s = shape_of(w)
+    o = hga.forward(s, t["Q"], t["K"], t["V"])
+    ws = torch.empty(hga.hga_attend_bwd_workspace(s), dtype=torch.uint8, device=DEV)
+    a = [torch.empty_like(t["Q"]), torch.empty_like(t["K"]), torch.empty_like(t["V"])]
+    hga.hga_attend_bwd(s, t["Q"], t["K"], t["V"], o["O"], o["lse"], t["dO"], o["group_idx"],
+                       *a, ws)
+    bq, bk, bv = (torch.empty_like(v) for v in a)
+    ws.fill_(0xFF)
+    hga.hga_attend_bwd_dq(s, t["Q"], t["K"], t["V"], o["O"], o["lse"], t["dO"], o["group_idx"],
+                          bq, ws)
+    hga.hga_attend_bwd_dkdv(s, t["Q"], t["K"], t["V"], o["lse"], t["dO"], o["group_idx"], bk, bv,
+                            ws)
+    torch.cuda.synchronize()
+    for x0, x1 in zip(a, (bq, bk, bv)):
+        assert torch.equal(x0, x1)
+
+
 def test_incremental_summaries_match_full_build():
     w = SMALL["bf16_seg_b2"]
     x = syn.make_inputs(w)
@@ -207,7 +230,8 @@ def test_full_size_forward_sampled_heads(oracle, name):
         assert_close(lse[b:b + 1, hq:hq + 1], lse_o, w.dtype, f"lse[{b},{hq}]")
 
 
-@pytest.mark.parametrize("name,b,hkv", [("segment_2k_over_16k", 0, 0), ("fwd_bwd_b2_4k", 1, 7)])
+@pytest.mark.parametrize("name,b,hkv", [("segment_2k_over_16k", 0, 0), ("fwd_bwd_b2_4k", 1, 7),
+                                        ("segment_2k_over_64k_ties", 0, 5)])
 def test_full_size_backward_sampled_kv_group(oracle, name, b, hkv):
     """dQ of the kv group's query heads and dK, dV of the kv head, at full size."""
     w, s, x, t, out = _full(name)
