@@ -55,6 +55,9 @@ def parse():
                     help="skip the CPU oracle leg (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--segments", action="store_true",
+                    help="segment-wise mode: the 16384-token sequence as 8 segments of 2048, "
+                         "each forward + backward with the history detached")
     return ap.parse_args()
 
 
@@ -134,6 +137,74 @@ def cpu_baseline(w, x, budget_s: float = 12.0):
     }
 
 
+def segments_main(args):
+    """Segment-wise training step of one layer: a 16384-token sequence cut into
+    8 segments of 2048 tokens, each running summaries (appended), routing,
+    attention forward and the backward (dQ; dK, dV of the segment's own keys
+    only) in order.  Reports the whole sequence's rate and each segment's time
+    against its offset."""
+    import torch
+    from hierarchical_routed_sparse_amd import synthetic as syn
+    from hierarchical_routed_sparse_amd.segments import SegmentRunner
+
+    L, S = 16384, 2048
+    w = syn.Workload("sequence_16k", 1, 32, 8, 128, L, L, 16, 64, "bf16", 5,
+                     1 / (128 ** 0.5), backward=True)
+    x = syn.make_inputs(w, with_grad_output=True)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t = {k: syn.to_torch(v, w.dtype, dev) for k, v in x.items()}
+    run = SegmentRunner(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, L, S, w.top_k, w.top_g,
+                        dtype=w.dtype, device=dev)
+    run.k_history.copy_(t["K"])
+    run.v_history.copy_(t["V"])
+    nseg = L // S
+    Qs = [t["Q"][:, :, i * S:(i + 1) * S].contiguous() for i in range(nseg)]
+    dOs = [t["dO"][:, :, i * S:(i + 1) * S].contiguous() for i in range(nseg)]
+    stream = torch.cuda.current_stream()
+
+    def one_pass(ev=None):
+        for i in range(nseg):
+            if ev: ev[i][0].record(stream)
+            run.step(i, Qs[i], dOs[i], stream=stream)
+            if ev: ev[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nseg)]
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        one_pass(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_pass = wall * 1e3 / args.steps
+    seg = [{"offset": i * S, "kv_len": (i + 1) * S,
+            "ms": round(sum(e[i][0].elapsed_time(e[i][1]) for e in evs) / args.steps, 4)}
+           for i in range(nseg)]
+    out = {
+        "metric": "HGA segment-wise fwd+bwd query tokens/sec, 16K sequence as 8 x 2048 segments "
+                  "(history detached), 1 MI355X",
+        "value": w.batch * L / (ms_pass * 1e-3),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_pass,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded clustered keys, N(0,1)/sqrt(128) queries and values)",
+        "config": {"workload": "sequence_16k as 8 segments of 2048, fwd+bwd per segment",
+                   "batch": 1, "q_heads": 32, "kv_heads": 8, "head_dim": 128, "seq_len": L,
+                   "segment": S, "top_k": 16, "top_g": 64},
+        "segments": seg,
+    }
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -141,6 +212,10 @@ def main():
               "(the layer shards by kv head with no exchange; see the design notes).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.segments:
+        segments_main(args)
+        return
 
     import torch
     import hierarchical_routed_sparse_amd as hga

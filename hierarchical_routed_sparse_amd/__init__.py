@@ -6,9 +6,9 @@ every step of the method runs in the library's HIP kernels.  Torch is used for
 device memory and streams.  If ``libhga.so`` has not been built, the first call
 raises ``HGAError``: there is no fallback implementation.
 
-Tensors: Q, O, dO, dQ [B,Hq,q_len,D]; K, V, dK, dV [B,Hkv,kv_len,D] of the
-shape's dtype (torch.bfloat16 or torch.float32); chunk_mean
-[B,Hkv,kv_len/64,D] and group_mean [B,Hkv,kv_len/8,D] float32; chunk_idx
+Tensors: Q, O, dO, dQ [B,Hq,q_len,D]; K, V, dK, dV [B,Hkv,C,D] of the
+shape's dtype (torch.bfloat16 or torch.float32), C = kv_capacity (kv_len when
+0); chunk_mean [B,Hkv,C/64,D] and group_mean [B,Hkv,C/8,D] float32; chunk_idx
 [B,Hq,q_len/64,top_k] and group_idx [B,Hq,q_len/64,top_g] int32; lse
 [B,Hq,q_len] float32.  All contiguous, on the current GPU.
 """
@@ -20,7 +20,8 @@ import os
 __all__ = [
     "HGAError", "HgaShape", "make_shape", "lib_path", "hga_abi_version", "hga_validate_shape",
     "hga_build_summaries", "hga_route", "hga_attend_fwd", "hga_attend_bwd_workspace",
-    "hga_attend_bwd", "hga_attend_bwd_dq", "hga_attend_bwd_dkdv", "forward", "backward",
+    "hga_attend_bwd", "hga_attend_bwd_dq", "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range",
+    "forward", "backward",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +43,7 @@ class HgaShape(ctypes.Structure):
         ("q_len", ctypes.c_int32), ("kv_len", ctypes.c_int32),
         ("top_k", ctypes.c_int32), ("top_g", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("kv_capacity", ctypes.c_int32),
     ]
 
     def __repr__(self):
@@ -50,10 +52,10 @@ class HgaShape(ctypes.Structure):
 
 
 def make_shape(batch, n_q_heads, n_kv_heads, head_dim, q_len, kv_len, top_k, top_g,
-               dtype="bf16", softmax_scale=0.0) -> HgaShape:
+               dtype="bf16", softmax_scale=0.0, kv_capacity=0) -> HgaShape:
     dt = {"bf16": HGA_DTYPE_BF16, "fp32": HGA_DTYPE_FP32}.get(dtype, dtype)
     return HgaShape(batch, n_q_heads, n_kv_heads, head_dim, q_len, kv_len, top_k, top_g,
-                    float(softmax_scale), int(dt))
+                    float(softmax_scale), int(dt), int(kv_capacity))
 
 
 _lib = None
@@ -84,9 +86,10 @@ def _load():
     lib.hga_attend_bwd.argtypes = [_SP] + [_vp] * 11 + [sz, _vp]
     lib.hga_attend_bwd_dq.argtypes = [_SP] + [_vp] * 9 + [sz, _vp]
     lib.hga_attend_bwd_dkdv.argtypes = [_SP] + [_vp] * 9 + [sz, _vp]
+    lib.hga_attend_bwd_dkdv_range.argtypes = [_SP] + [_vp] * 6 + [i32, i32] + [_vp] * 3 + [sz, _vp]
     for name in ("hga_validate_shape", "hga_build_summaries", "hga_route", "hga_attend_fwd",
                  "hga_attend_bwd_workspace", "hga_attend_bwd", "hga_attend_bwd_dq",
-                 "hga_attend_bwd_dkdv"):
+                 "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -130,13 +133,19 @@ def _ptr(t, name, dtype=None, size=None, nullable=False):
     return t.data_ptr()
 
 
+def capacity(s: HgaShape) -> int:
+    """Key/value rows allocated per (b, kv head)."""
+    return s.kv_capacity if s.kv_capacity > 0 else s.kv_len
+
+
 def _sizes(s: HgaShape):
     nblk = s.q_len // QBLOCK
+    cap = capacity(s)
     return dict(
         q=(s.batch, s.n_q_heads, s.q_len, s.head_dim),
-        kv=(s.batch, s.n_kv_heads, s.kv_len, s.head_dim),
-        cm=(s.batch, s.n_kv_heads, s.kv_len // CHUNK, s.head_dim),
-        gm=(s.batch, s.n_kv_heads, s.kv_len // GROUP, s.head_dim),
+        kv=(s.batch, s.n_kv_heads, cap, s.head_dim),
+        cm=(s.batch, s.n_kv_heads, cap // CHUNK, s.head_dim),
+        gm=(s.batch, s.n_kv_heads, cap // GROUP, s.head_dim),
         ci=(s.batch, s.n_q_heads, nblk, s.top_k),
         gi=(s.batch, s.n_q_heads, nblk, s.top_g),
         lse=(s.batch, s.n_q_heads, s.q_len),
@@ -239,6 +248,21 @@ def hga_attend_bwd_dkdv(shape, Q, K, V, lse, dO, group_idx, dK, dV, workspace, s
         _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
         _ptr(dK, "dK", dt, sz["kv"]), _ptr(dV, "dV", dt, sz["kv"]), wp, wb, _stream(stream)),
         "hga_attend_bwd_dkdv")
+
+
+def hga_attend_bwd_dkdv_range(shape, Q, K, V, lse, dO, group_idx, chunk_begin, chunk_end, dK, dV,
+                              workspace, stream=None):
+    import torch
+    sz, dt = _sizes(shape), _elt_dtype(shape)
+    wp, wb = _ws(workspace)
+    _check(_load().hga_attend_bwd_dkdv_range(
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"]),
+        _ptr(V, "V", dt, sz["kv"]), _ptr(lse, "lse", torch.float32, sz["lse"]),
+        _ptr(dO, "dO", dt, sz["q"]),
+        _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        int(chunk_begin), int(chunk_end),
+        _ptr(dK, "dK", dt, sz["kv"]), _ptr(dV, "dV", dt, sz["kv"]), wp, wb, _stream(stream)),
+        "hga_attend_bwd_dkdv_range")
 
 
 # ------------------------------------------------------------------ compositions

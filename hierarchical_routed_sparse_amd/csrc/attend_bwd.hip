@@ -82,7 +82,7 @@ struct DqP {
   void* dQ;
   float* delta;
   uint8_t* cmask;   // [routing row][chunk] kept-group masks, for the dK/dV kernel
-  int B, Hq, Hkv, Sq, Skv, q0, nblk, top_g, nwork;
+  int B, Hq, Hkv, Sq, Skv, Scap, q0, nblk, top_g, nwork;
   float scale;
 };
 
@@ -128,8 +128,8 @@ void attend_bwd_dq_kernel(const DqP p) {
   const int nvalid = load_routing_row(p.gidx + row * p.top_g, p.top_g, cb, s_glist, s_wsum);
   const int ntiles = kLocalTiles + (nvalid + kGroupsPerTile - 1) / kGroupsPerTile;
 
-  const T* Kbh = reinterpret_cast<const T*>(p.K) + (long long)bh * p.Skv * D;
-  const T* Vbh = reinterpret_cast<const T*>(p.V) + (long long)bh * p.Skv * D;
+  const T* Kbh = reinterpret_cast<const T*>(p.K) + (long long)bh * p.Scap * D;
+  const T* Vbh = reinterpret_cast<const T*>(p.V) + (long long)bh * p.Scap * D;
   const long long qrow0 = ((long long)b * p.Hq + hq) * p.Sq + (long long)blk * kChunk;
   const int qq = 16 * wv + l16;
 
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
   const int l16 = lane & 15, g4 = lane >> 4;
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = w / p.nchunks, c = w % p.nchunks;
+  const int bh = w / p.nrange, c = p.chunk0 + w % p.nrange;
   const int b = bh / p.Hkv, hkv = bh % p.Hkv;
   const int r = p.Hq / p.Hkv;
   const int nrows = r * p.nblk;          // (query head in group, block), head-major
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
   // this wavefront's 16 keys as B operands of S = Q . K^T and dP = dO . V^T
   Frag<T> kf[D / 32], vf[D / 32];
   {
-    const long long off = ((long long)bh * p.Skv + (long long)c * kChunk + kin) * D + 8 * g4;
+    const long long off = ((long long)bh * p.Scap + (long long)c * kChunk + kin) * D + 8 * g4;
     const T* k = reinterpret_cast<const T*>(p.K) + off;
     const T* v = reinterpret_cast<const T*>(p.V) + off;
 #pragma unroll
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
   }
 
   // every key of the chunk is written (zero when nothing attends it)
-  const long long krow = (long long)bh * p.Skv + (long long)c * kChunk + kin;
+  const long long krow = (long long)bh * p.Scap + (long long)c * kChunk + kin;
   T* dk = reinterpret_cast<T*>(p.dK) + krow * D + 4 * g4;
   T* dv = reinterpret_cast<T*>(p.dV) + krow * D + 4 * g4;
   const float sc = p.scale;
@@ -538,7 +538,7 @@ hipError_t run_dq(const Dims& d, const void* Q, const void* K, const void* V, co
   DqP p;
   p.Q = Q; p.K = K; p.V = V; p.O = O; p.lse = lse; p.dO = dO; p.gidx = gi; p.dQ = dQ;
   p.delta = delta; p.cmask = cmask;
-  p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.q0 = d.q0;
+  p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.Scap = d.Scap; p.q0 = d.q0;
   p.nblk = d.nblk; p.top_g = d.top_g; p.scale = d.scale;
   p.nwork = d.B * d.Hq * d.nblk;
   constexpr int TK = HGA_DQ_TILE;
@@ -553,15 +553,17 @@ hipError_t run_dq(const Dims& d, const void* Q, const void* K, const void* V, co
 template <typename T, int D>
 hipError_t run_dkdv(const Dims& d, const void* Q, const void* K, const void* V, const float* lse,
                     const void* dO, const int32_t* gi, const float* delta, const uint8_t* cmask,
-                    void* dK, void* dV, hipStream_t s) {
+                    void* dK, void* dV, int chunk_begin, int chunk_end, hipStream_t s) {
   DkvP p;
   p.Q = Q; p.K = K; p.V = V; p.lse = lse; p.dO = dO; p.gidx = gi; p.delta = delta;
   p.cmask = cmask;
   p.dK = dK; p.dV = dV;
-  p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.q0 = d.q0;
+  p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.Scap = d.Scap; p.q0 = d.q0;
   p.nblk = d.nblk; p.top_g = d.top_g; p.scale = d.scale;
   p.nchunks = d.Skv / kChunk;
-  p.nwork = d.B * d.Hkv * p.nchunks;
+  p.chunk0 = chunk_begin;
+  p.nrange = chunk_end - chunk_begin;
+  p.nwork = d.B * d.Hkv * p.nrange;
   constexpr int kStageBytes = 2 * 64 * D * (int)sizeof(T) + 512;
   constexpr int S0 = HGA_DKV_STAGES;
   constexpr int S = S0 * kStageBytes <= 140 * 1024 ? S0 : (140 * 1024) / kStageBytes;
@@ -586,12 +588,12 @@ hipError_t launch_attend_bwd_dq(const Dims& d, const void* Q, const void* K, con
 hipError_t launch_attend_bwd_dkdv(const Dims& d, const void* Q, const void* K, const void* V,
                                   const float* lse, const void* dO, const int32_t* group_idx,
                                   const float* delta, const uint8_t* cmask, void* dK, void* dV,
-                                  hipStream_t s) {
+                                  int chunk_begin, int chunk_end, hipStream_t s) {
   if (d.bf16)
-    return d.D == 128 ? run_dkdv<uint16_t, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, s)
-                      : run_dkdv<uint16_t, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, s);
-  return d.D == 128 ? run_dkdv<float, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, s)
-                    : run_dkdv<float, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, s);
+    return d.D == 128 ? run_dkdv<uint16_t, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, chunk_begin, chunk_end, s)
+                      : run_dkdv<uint16_t, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, chunk_begin, chunk_end, s);
+  return d.D == 128 ? run_dkdv<float, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, chunk_begin, chunk_end, s)
+                    : run_dkdv<float, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, chunk_begin, chunk_end, s);
 }
 
 }  // namespace hga

@@ -42,7 +42,7 @@ struct FwdP {
   const int32_t* gidx;
   void* O;
   float* lse;
-  int B, Hq, Hkv, Sq, Skv, q0, nblk, top_g, nwork;
+  int B, Hq, Hkv, Sq, Skv, Scap, q0, nblk, top_g, nwork;
   float scale;
 };
 
@@ -105,8 +105,8 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
   }
   const int ntiles = kLocalTiles + (nvalid + kGroupsPerTile - 1) / kGroupsPerTile;
 
-  const T* Kbh = reinterpret_cast<const T*>(p.K) + (long long)bh * p.Skv * D;
-  const T* Vbh = reinterpret_cast<const T*>(p.V) + (long long)bh * p.Skv * D;
+  const T* Kbh = reinterpret_cast<const T*>(p.K) + (long long)bh * p.Scap * D;
+  const T* Vbh = reinterpret_cast<const T*>(p.V) + (long long)bh * p.Scap * D;
   const long long qrow0 = ((long long)b * p.Hq + hq) * p.Sq + (long long)blk * kChunk;
 
   // this wavefront's 16 queries as B operands of S^T = K . Q^T
@@ -293,7 +293,7 @@ hipError_t run(const Dims& d, const void* Q, const void* K, const void* V, const
                void* O, float* lse, hipStream_t s) {
   FwdP p;
   p.Q = Q; p.K = K; p.V = V; p.gidx = gi; p.O = O; p.lse = lse;
-  p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.q0 = d.q0;
+  p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.Scap = d.Scap; p.q0 = d.q0;
   p.nblk = d.nblk; p.top_g = d.top_g; p.scale = d.scale;
   p.nwork = d.B * d.Hq * d.nblk;
   // fp32 tiles are twice as large: cap the stages at 128 KB of LDS

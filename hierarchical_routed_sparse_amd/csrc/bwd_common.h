@@ -16,7 +16,8 @@ struct DkvP {
   const uint8_t* cmask;   // [routing row][chunk] kept-group masks (from the dQ kernel)
   void* dK;
   void* dV;
-  int B, Hq, Hkv, Sq, Skv, q0, nblk, top_g, nchunks, nwork;
+  int B, Hq, Hkv, Sq, Skv, Scap, q0, nblk, top_g, nchunks, nwork;
+  int chunk0, nrange;   // the workgroups cover chunks [chunk0, chunk0 + nrange)
   float scale;
 };
 

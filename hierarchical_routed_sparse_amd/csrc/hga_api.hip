@@ -17,6 +17,7 @@ hga::Dims dims_of(const hga_shape* s) {
   d.D = s->head_dim;
   d.Sq = s->q_len;
   d.Skv = s->kv_len;
+  d.Scap = s->kv_capacity > 0 ? s->kv_capacity : s->kv_len;
   d.top_k = s->top_k;
   d.top_g = s->top_g;
   d.q0 = s->kv_len - s->q_len;
@@ -66,6 +67,9 @@ hga_status hga_validate_shape(const hga_shape* s) {
   if (s->q_len < HGA_QBLOCK || s->q_len % HGA_QBLOCK != 0) return HGA_ERR_SHAPE;
   if (s->kv_len % HGA_CHUNK != 0 || s->kv_len < s->q_len || s->kv_len > HGA_MAX_KV_LEN)
     return HGA_ERR_SHAPE;
+  if (s->kv_capacity != 0 && (s->kv_capacity < s->kv_len || s->kv_capacity % HGA_CHUNK != 0 ||
+                              s->kv_capacity > HGA_MAX_KV_LEN))
+    return HGA_ERR_SHAPE;
   if (s->top_k < 0 || s->top_k > HGA_MAX_TOP_K) return HGA_ERR_SHAPE;
   if (s->top_g < 0 || s->top_g > HGA_MAX_TOP_G) return HGA_ERR_SHAPE;
   // NaN or infinite scale (checked on the bit pattern: the library is built
@@ -77,7 +81,8 @@ hga_status hga_validate_shape(const hga_shape* s) {
   if (s->dtype != HGA_DTYPE_BF16 && s->dtype != HGA_DTYPE_FP32) return HGA_ERR_UNSUPPORTED;
   // launch sizes must fit a 32-bit grid
   const long long rows = (long long)s->batch * s->n_q_heads * (s->q_len / HGA_QBLOCK);
-  const long long chunks = (long long)s->batch * s->n_kv_heads * (s->kv_len / HGA_CHUNK);
+  const long long cap = s->kv_capacity > 0 ? s->kv_capacity : s->kv_len;
+  const long long chunks = (long long)s->batch * s->n_kv_heads * (cap / HGA_CHUNK);
   if (rows > (1LL << 30) || chunks > (1LL << 30)) return HGA_ERR_SHAPE;
   // routing rows of one kv head must fit the 23-bit row field of the backward entry list
   if ((long long)(s->n_q_heads / s->n_kv_heads) * (s->q_len / HGA_QBLOCK) >= (1LL << 23))
@@ -144,18 +149,32 @@ hga_status hga_attend_bwd_dq(const hga_shape* shape, const void* Q, const void* 
       (uint8_t*)workspace + delta_bytes(shape), (hipStream_t)stream));
 }
 
-hga_status hga_attend_bwd_dkdv(const hga_shape* shape, const void* Q, const void* K,
-                               const void* V, const float* lse, const void* dO,
-                               const int32_t* group_idx, void* dK, void* dV,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+hga_status hga_attend_bwd_dkdv_range(const hga_shape* shape, const void* Q, const void* K,
+                                     const void* V, const float* lse, const void* dO,
+                                     const int32_t* group_idx, int32_t chunk_begin,
+                                     int32_t chunk_end, void* dK, void* dV, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
   hga_status st = hga_validate_shape(shape);
   if (st != HGA_OK) return st;
   if (!Q || !K || !V || !lse || !dO || !dK || !dV) return HGA_ERR_NULL;
   if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
   if (!workspace || workspace_bytes < ::workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
+  if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > shape->kv_len / HGA_CHUNK)
+    return HGA_ERR_SHAPE;
+  if (chunk_end == chunk_begin) return HGA_OK;
   return from_hip(hga::launch_attend_bwd_dkdv(
       dims_of(shape), Q, K, V, lse, dO, group_idx, (const float*)workspace,
-      (const uint8_t*)workspace + delta_bytes(shape), dK, dV, (hipStream_t)stream));
+      (const uint8_t*)workspace + delta_bytes(shape), dK, dV, chunk_begin, chunk_end,
+      (hipStream_t)stream));
+}
+
+hga_status hga_attend_bwd_dkdv(const hga_shape* shape, const void* Q, const void* K,
+                               const void* V, const float* lse, const void* dO,
+                               const int32_t* group_idx, void* dK, void* dV,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  const int32_t nch = shape ? shape->kv_len / HGA_CHUNK : 0;
+  return hga_attend_bwd_dkdv_range(shape, Q, K, V, lse, dO, group_idx, 0, nch, dK, dV,
+                                   workspace, workspace_bytes, stream);
 }
 
 hga_status hga_attend_bwd(const hga_shape* shape, const void* Q, const void* K, const void* V,

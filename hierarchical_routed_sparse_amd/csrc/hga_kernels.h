@@ -9,6 +9,7 @@ namespace hga {
 
 struct Dims {
   int B, Hq, Hkv, D, Sq, Skv, top_k, top_g;
+  int Scap;    // rows allocated per (b, kv head) in K, V, dK, dV (>= Skv)
   int q0;      // Skv - Sq: absolute position of the first query
   int nblk;    // Sq / 64
   float scale; // softmax scale
@@ -33,6 +34,6 @@ hipError_t launch_attend_bwd_dq(const Dims& d, const void* Q, const void* K, con
 hipError_t launch_attend_bwd_dkdv(const Dims& d, const void* Q, const void* K, const void* V,
                                   const float* lse, const void* dO, const int32_t* group_idx,
                                   const float* delta, const uint8_t* cmask, void* dK, void* dV,
-                                  hipStream_t s);
+                                  int chunk_begin, int chunk_end, hipStream_t s);
 
 }  // namespace hga

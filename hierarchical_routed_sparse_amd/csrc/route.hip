@@ -39,7 +39,7 @@ struct RouteP {
   const float* gm;
   int32_t* cidx;
   int32_t* gidx;
-  int B, Hq, Hkv, Sq, Skv, q0, nblk, top_k, top_g, nsets, nwork;
+  int B, Hq, Hkv, Sq, Skv, Scap, q0, nblk, top_k, top_g, nsets, nwork;
 };
 
 // Order-preserving map from finite fp32 to uint32 (larger float -> larger key).
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
   const int h0 = set * kRowsPerWG;                       // first query head of the set (within the group)
   const int nrows = min(kRowsPerWG, r - h0);             // rows of this set
   const int cb = p.q0 / kChunk + blk;                    // the block's own chunk = number of candidates
-  const long long nch = p.Skv / kChunk;
+  const long long nch = p.Scap / kChunk;   // chunk rows per (b, kv head) in the summaries
 
   // 1. block query of row wv (head hkv*r + h0 + wv): lane (o = l%16, rg = l/16)
   //    sums rows 16rg..16rg+15 of columns 8o..8o+7
@@ -293,7 +293,7 @@ hipError_t run(const Dims& d, const void* Q, const float* cm, const float* gm, i
                int32_t* gi, hipStream_t s) {
   RouteP p;
   p.Q = Q; p.cm = cm; p.gm = gm; p.cidx = ci; p.gidx = gi;
-  p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.q0 = d.q0;
+  p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.Scap = d.Scap; p.q0 = d.q0;
   p.nblk = d.nblk; p.top_k = d.top_k; p.top_g = d.top_g;
   const int r = d.Hq / d.Hkv;
   p.nsets = (r + kRowsPerWG - 1) / kRowsPerWG;

@@ -20,7 +20,7 @@ struct SumP {
   const void* K;
   float* cm;
   float* gm;
-  int Skv, chunk_begin, chunk_end, nslots, nwork;
+  int Scap, chunk_begin, chunk_end, nslots, nwork;   // Scap: rows per (b, kv head)
 };
 
 template <typename T, int D>
@@ -37,14 +37,14 @@ __global__ __launch_bounds__(kThreads) void summaries_kernel(const SumP p) {
   const int chunk = p.chunk_begin + (w % p.nslots) * kCpw + lc;
   const int pr = tid % kPpc, q = pr / kOct, o = pr % kOct;
   const bool live = chunk < p.chunk_end;
-  const long long nch = p.Skv / kChunk;
+  const long long nch = p.Scap / kChunk;   // chunk rows per (b, kv head) in the summaries
 
   float s[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = 0.f;
   if (live) {
     Pair<T> x;
-    load_pair(x, reinterpret_cast<const T*>(p.K) + ((long long)bh * p.Skv + chunk * kChunk + 4 * q) * D + 8 * o, D);
+    load_pair(x, reinterpret_cast<const T*>(p.K) + ((long long)bh * p.Scap + chunk * kChunk + 4 * q) * D + 8 * o, D);
     const T* r = reinterpret_cast<const T*>(&x);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -79,7 +79,7 @@ template <typename T, int D>
 hipError_t run(const Dims& d, const void* K, float* cm, float* gm, int cb, int ce, hipStream_t s) {
   constexpr int kCpw = kThreads / (16 * (D / 8));
   SumP p;
-  p.K = K; p.cm = cm; p.gm = gm; p.Skv = d.Skv; p.chunk_begin = cb; p.chunk_end = ce;
+  p.K = K; p.cm = cm; p.gm = gm; p.Scap = d.Scap; p.chunk_begin = cb; p.chunk_end = ce;
   p.nslots = (ce - cb + kCpw - 1) / kCpw;
   p.nwork = d.B * d.Hkv * p.nslots;
   if (p.nwork == 0) return hipSuccess;

@@ -1,0 +1,112 @@
+"""Segment-wise HGA over a long sequence (truncated backpropagation through time).
+
+Page "BMW's 16 GB GPU just did what needs an A100", section "What HGA does
+differently": the sequence is cut into segments (2,048 tokens there) that run
+forward and backward one after another; the summaries of earlier chunks stay
+resident, later segments still route to and attend the exact tokens of
+earlier ones, and the earlier keys and values are detached, so no gradient
+reaches them.
+
+``SegmentRunner`` holds one attention layer's key/value history and its chunk
+and group summaries in buffers sized once for the whole sequence (the shape's
+``kv_capacity``).  For segment ``i`` (positions ``[i*S, (i+1)*S)``) it
+
+1. appends the summaries of the segment's chunks (``hga_build_summaries``
+   over chunks ``[i*S/64, (i+1)*S/64)``; the older ones are not rebuilt);
+2. routes the segment's queries over everything up to the segment's end
+   (``kv_len = (i+1)*S``);
+3. runs the exact-token attention forward;
+4. runs the backward: dQ of the segment's queries, and dK, dV of the
+   segment's own keys only (``hga_attend_bwd_dkdv_range``): history rows of
+   dK, dV are neither computed nor written.
+
+Every step is a call of the C ABI; this module only sequences them and owns
+the buffers.  The caller writes a segment's keys and values into
+``k_history[:, :, i*S:(i+1)*S]`` (and the same for ``v_history``) before
+calling ``step(i, ...)``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from . import (CHUNK, hga_attend_bwd_dkdv_range, hga_attend_bwd_dq, hga_attend_bwd_workspace,
+               hga_attend_fwd, hga_build_summaries, hga_route, make_shape)
+
+
+@dataclass
+class SegmentResult:
+    O: object            # [B, Hq, S, D]
+    lse: object          # [B, Hq, S]
+    group_idx: object    # [B, Hq, S/64, top_g]
+    dQ: object           # [B, Hq, S, D]
+    dK: object           # view [B, Hkv, S, D] of the segment's rows
+    dV: object           # view [B, Hkv, S, D] of the segment's rows
+
+
+class SegmentRunner:
+    def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int,
+                 seg_len: int, top_k: int, top_g: int, dtype: str = "bf16",
+                 softmax_scale: float = 0.0, device="cuda:0"):
+        import torch
+        if seg_len % CHUNK or seq_len % seg_len:
+            raise ValueError("seg_len must be a multiple of 64 dividing seq_len")
+        self.B, self.Hq, self.Hkv, self.D = batch, n_q_heads, n_kv_heads, head_dim
+        self.L, self.S, self.top_k, self.top_g = seq_len, seg_len, top_k, top_g
+        self.dtype, self.scale = dtype, softmax_scale
+        self.nseg = seq_len // seg_len
+        elt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        f32, i32 = torch.float32, torch.int32
+        kv = (batch, n_kv_heads, seq_len, head_dim)
+        q = (batch, n_q_heads, seg_len, head_dim)
+        nblk = seg_len // 64
+        self.k_history = torch.zeros(kv, dtype=elt, device=device)
+        self.v_history = torch.zeros(kv, dtype=elt, device=device)
+        self.chunk_mean = torch.zeros(batch, n_kv_heads, seq_len // 64, head_dim, dtype=f32,
+                                      device=device)
+        self.group_mean = torch.zeros(batch, n_kv_heads, seq_len // 8, head_dim, dtype=f32,
+                                      device=device)
+        self.chunk_idx = torch.empty(batch, n_q_heads, nblk, top_k, dtype=i32, device=device)
+        self.group_idx = torch.empty(batch, n_q_heads, nblk, top_g, dtype=i32, device=device)
+        self.O = torch.empty(q, dtype=elt, device=device)
+        self.lse = torch.empty(batch, n_q_heads, seg_len, dtype=f32, device=device)
+        self.dQ = torch.empty(q, dtype=elt, device=device)
+        self.dK = torch.zeros(kv, dtype=elt, device=device)
+        self.dV = torch.zeros(kv, dtype=elt, device=device)
+        # the last segment needs the largest workspace (longest history)
+        self.workspace = torch.empty(hga_attend_bwd_workspace(self.shape(self.nseg - 1)),
+                                     dtype=torch.uint8, device=device)
+
+    def shape(self, i: int):
+        """Shape of segment i: q_len = S at the end of kv_len = (i+1) S."""
+        return make_shape(self.B, self.Hq, self.Hkv, self.D, self.S, (i + 1) * self.S,
+                          self.top_k, self.top_g, dtype=self.dtype,
+                          softmax_scale=self.scale, kv_capacity=self.L)
+
+    def forward(self, i: int, Q, stream=None):
+        """Steps 1-3 for segment i (its keys/values already in the history)."""
+        s = self.shape(i)
+        c0, c1 = i * self.S // CHUNK, (i + 1) * self.S // CHUNK
+        hga_build_summaries(s, self.k_history, self.chunk_mean, self.group_mean, c0, c1,
+                            stream=stream)
+        hga_route(s, Q, self.chunk_mean, self.group_mean, self.chunk_idx, self.group_idx,
+                  stream=stream)
+        hga_attend_fwd(s, Q, self.k_history, self.v_history, self.group_idx, self.O, self.lse,
+                       stream=stream)
+
+    def backward(self, i: int, Q, dO, stream=None):
+        """Step 4 for segment i, after forward(i, Q): dQ, and dK, dV of the
+        segment's own keys (history detached)."""
+        s = self.shape(i)
+        c0, c1 = i * self.S // CHUNK, (i + 1) * self.S // CHUNK
+        hga_attend_bwd_dq(s, Q, self.k_history, self.v_history, self.O, self.lse, dO,
+                          self.group_idx, self.dQ, self.workspace, stream=stream)
+        hga_attend_bwd_dkdv_range(s, Q, self.k_history, self.v_history, self.lse, dO,
+                                  self.group_idx, c0, c1, self.dK, self.dV, self.workspace,
+                                  stream=stream)
+
+    def step(self, i: int, Q, dO, stream=None) -> SegmentResult:
+        self.forward(i, Q, stream)
+        self.backward(i, Q, dO, stream)
+        rows = slice(i * self.S, (i + 1) * self.S)
+        return SegmentResult(self.O, self.lse, self.group_idx, self.dQ,
+                             self.dK[:, :, rows], self.dV[:, :, rows])

@@ -27,10 +27,14 @@
  * Conventions for every call:
  *   - all tensor pointers are DEVICE pointers to contiguous row-major buffers
  *     owned by the caller, 16-byte aligned; outputs must not alias inputs;
- *   - Q, O, dO, dQ are [B][Hq][q_len][D]; K, V, dK, dV are [B][Hkv][kv_len][D];
- *     the q_len queries are the LAST q_len positions of the kv_len-long
- *     sequence (a segment at the end of its history; q_len == kv_len is plain
- *     causal self-attention);
+ *   - Q, O, dO, dQ are [B][Hq][q_len][D]; K, V, dK, dV are [B][Hkv][C][D]
+ *     with C = kv_capacity (kv_len when 0): rows kv_len..C-1 of each
+ *     (b, kv head) are not read, so a history that grows segment by segment
+ *     can live in buffers sized once; the q_len queries are the LAST q_len
+ *     positions of the kv_len-long sequence (a segment at the end of its
+ *     history; q_len == kv_len is plain causal self-attention);
+ *   - the summaries are [B][Hkv][C/64][D] (chunks) and [B][Hkv][C/8][D]
+ *     (groups), rows past kv_len/64 (kv_len/8) unused;
  *   - element type of Q, K, V, O, dO, dQ, dK, dV is shape->dtype (bf16 or fp32);
  *     summaries, lse and the workspace are fp32; indices are int32;
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); every
@@ -51,7 +55,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 1
+#define HGA_ABI_VERSION 2
 #define HGA_CHUNK 64      /* tokens per chunk (the page's 64-token chunks) */
 #define HGA_GROUP 8       /* tokens per group (the page's 8-token groups)  */
 #define HGA_QBLOCK 64     /* queries per routing block                      */
@@ -81,6 +85,9 @@ typedef struct {
   int32_t top_g;        /* groups kept per block, 0..HGA_MAX_TOP_G            */
   float softmax_scale;  /* <= 0 selects 1/sqrt(head_dim)                      */
   int32_t dtype;        /* hga_dtype                                          */
+  int32_t kv_capacity;  /* rows allocated per (b, kv head) in K, V, dK, dV:   */
+                        /* 0 (= kv_len) or a multiple of 64 in                */
+                        /* [kv_len, HGA_MAX_KV_LEN]                           */
 } hga_shape;
 
 /* ABI version (HGA_ABI_VERSION of the built library). */
@@ -95,10 +102,10 @@ hga_status hga_validate_shape(const hga_shape* shape);
 /* Chunk and group summaries of K (page section "What HGA does differently":
  * one compact summary vector per 64-token chunk stays resident in GPU memory;
  * the 8-token group summaries serve the second routing level).
- *   K          [B][Hkv][kv_len][D]           dtype
- *   chunk_mean [B][Hkv][kv_len/64][D]        fp32, written for chunks in
+ *   K          [B][Hkv][C][D]                dtype (C = kv_capacity or kv_len)
+ *   chunk_mean [B][Hkv][C/64][D]             fp32, written for chunks in
  *                                            [chunk_begin, chunk_end) only
- *   group_mean [B][Hkv][kv_len/8][D]         fp32, written for the groups of
+ *   group_mean [B][Hkv][C/8][D]              fp32, written for the groups of
  *                                            those chunks only
  * 0 <= chunk_begin <= chunk_end <= kv_len/64.  The range lets a caller append
  * the summaries of new chunks to a resident history without rebuilding it. */
@@ -148,8 +155,8 @@ hga_status hga_attend_bwd_workspace(const hga_shape* shape, size_t* bytes);
  *   O, lse     outputs of hga_attend_fwd for the same inputs
  *   dO         [B][Hq][q_len][D]   dtype
  *   dQ         [B][Hq][q_len][D]   dtype
- *   dK, dV     [B][Hkv][kv_len][D] dtype; every position is written (zero
- *              where no query attends); the sum over the Hq/Hkv query heads
+ *   dK, dV     [B][Hkv][C][D] dtype; every position below kv_len is written
+ *              (zero where no query attends); the sum over the Hq/Hkv query heads
  *              of a kv head is formed in a fixed order, so results are
  *              bitwise reproducible
  *   workspace  device buffer of at least hga_attend_bwd_workspace() bytes */
@@ -172,6 +179,21 @@ hga_status hga_attend_bwd_dkdv(const hga_shape* shape, const void* Q, const void
                                const void* V, const float* lse, const void* dO,
                                const int32_t* group_idx, void* dK, void* dV,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* hga_attend_bwd_dkdv restricted to the keys of chunks [chunk_begin,
+ * chunk_end): only those rows of dK and dV are written (every row in the
+ * range, zero where no query attends); the other rows are left untouched and
+ * cost nothing.  This is the backward of segment-wise training (page section
+ * "What HGA does differently": each 2,048-token segment runs forward and
+ * backward on its own and older keys/values are detached), where only the
+ * segment's own keys take gradients: chunk_begin = (kv_len - q_len) / 64,
+ * chunk_end = kv_len / 64.  0 <= chunk_begin <= chunk_end <= kv_len / 64.
+ * Same workspace contract as hga_attend_bwd_dkdv. */
+hga_status hga_attend_bwd_dkdv_range(const hga_shape* shape, const void* Q, const void* K,
+                                     const void* V, const float* lse, const void* dO,
+                                     const int32_t* group_idx, int32_t chunk_begin,
+                                     int32_t chunk_end, void* dK, void* dV, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

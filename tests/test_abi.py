@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert hga.hga_abi_version() == 1
+    assert hga.hga_abi_version() == 2
 
 
 def _ok_shape(**kw):
@@ -63,6 +63,11 @@ def _ok_shape(**kw):
     ({"softmax_scale": float("nan")}, 2),
     ({"softmax_scale": float("inf")}, 2),
     ({"softmax_scale": -1.0}, 0),                 # <= 0 selects 1/sqrt(head_dim)
+    ({"kv_capacity": 32768}, 0),                  # rows allocated beyond kv_len
+    ({"kv_capacity": 16384}, 0),                  # equal to kv_len
+    ({"kv_capacity": 8192}, 2),                   # smaller than kv_len
+    ({"kv_capacity": 16400}, 2),                  # not a multiple of 64
+    ({"kv_capacity": 262144}, 2),                 # beyond the maximum
 ])
 def test_validate_shape(kw, status):
     assert hga.hga_validate_shape(_ok_shape(**kw)) == status
@@ -86,6 +91,17 @@ def test_null_and_workspace_errors_before_launch(lib):
     args = [16] * 11
     assert lib.hga_attend_bwd(ctypes.byref(s), *args[:10], None, need, None) == 4
     assert lib.hga_attend_bwd(ctypes.byref(s), *args, need - 1, None) == 4
+    # the workspace holds delta and the one-byte-per-(routing row, chunk) group map
+    nblk, nch = 2048 // 64, 16384 // 64
+    assert need == 4 * 32 * 2048 + 32 * nblk * nch
+    lib.hga_attend_bwd_dkdv_range.argtypes = ([SP] + [ctypes.c_void_p] * 6 + [ctypes.c_int32] * 2
+                                              + [ctypes.c_void_p] * 3 + [ctypes.c_size_t,
+                                                                         ctypes.c_void_p])
+    rng = [16] * 6
+    assert lib.hga_attend_bwd_dkdv_range(ctypes.byref(s), *rng, 5, 4, 16, 16, 16, need, None) == 2
+    assert lib.hga_attend_bwd_dkdv_range(ctypes.byref(s), *rng, 0, nch + 1, 16, 16, 16, need,
+                                         None) == 2
+    assert lib.hga_attend_bwd_dkdv_range(ctypes.byref(s), *rng, 7, 7, 16, 16, 16, need, None) == 0
     assert lib.hga_validate_shape(None) == 1
 
 
