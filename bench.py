@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--segments", action="store_true",
                     help="segment-wise mode: the 16384-token sequence as 8 segments of 2048, "
                          "each forward + backward with the history detached")
+    ap.add_argument("--host-kv", action="store_true",
+                    help="with --segments: keep the key/value history in pinned host memory")
     return ap.parse_args()
 
 
@@ -155,9 +157,9 @@ def segments_main(args):
     torch.cuda.set_device(0)
     t = {k: syn.to_torch(v, w.dtype, dev) for k, v in x.items()}
     run = SegmentRunner(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, L, S, w.top_k, w.top_g,
-                        dtype=w.dtype, device=dev)
-    run.k_history.copy_(t["K"])
-    run.v_history.copy_(t["V"])
+                        dtype=w.dtype, device=dev, kv_on_host=args.host_kv)
+    run.k_history.copy_(t["K"].cpu() if args.host_kv else t["K"])
+    run.v_history.copy_(t["V"].cpu() if args.host_kv else t["V"])
     nseg = L // S
     Qs = [t["Q"][:, :, i * S:(i + 1) * S].contiguous() for i in range(nseg)]
     dOs = [t["dO"][:, :, i * S:(i + 1) * S].contiguous() for i in range(nseg)]
@@ -183,9 +185,22 @@ def segments_main(args):
     seg = [{"offset": i * S, "kv_len": (i + 1) * S,
             "ms": round(sum(e[i][0].elapsed_time(e[i][1]) for e in evs) / args.steps, 4)}
            for i in range(nseg)]
+    # key/value rows each segment reads (one untimed pass): the forward and the
+    # dQ pass each gather every row's kept groups and own chunk; summaries and
+    # dK/dV read the segment's own keys (and values)
+    row_bytes = w.head_dim * 2
+    for i in range(nseg):
+        run.forward(i, Qs[i], stream=stream)
+        kept = int((run.group_idx >= 0).sum().item())
+        rows = w.batch * w.n_q_heads * (S // 64)
+        gather = (kept * 8 + rows * 64) * row_bytes * 2
+        own = w.batch * w.n_kv_heads * S * row_bytes
+        seg[i]["kv_bytes_read"] = 2 * gather + own + 2 * own
+        seg[i]["kv_GBs"] = round(seg[i]["kv_bytes_read"] / (seg[i]["ms"] * 1e-3) / 1e9, 1)
     out = {
         "metric": "HGA segment-wise fwd+bwd query tokens/sec, 16K sequence as 8 x 2048 segments "
-                  "(history detached), 1 MI355X",
+                  "(history detached" + (", K/V in pinned host memory" if args.host_kv else "")
+                  + "), 1 MI355X",
         "value": w.batch * L / (ms_pass * 1e-3),
         "unit": "query tokens/s",
         "n_gpus": 1,

@@ -10,7 +10,10 @@ Tensors: Q, O, dO, dQ [B,Hq,q_len,D]; K, V, dK, dV [B,Hkv,C,D] of the
 shape's dtype (torch.bfloat16 or torch.float32), C = kv_capacity (kv_len when
 0); chunk_mean [B,Hkv,C/64,D] and group_mean [B,Hkv,C/8,D] float32; chunk_idx
 [B,Hq,q_len/64,top_k] and group_idx [B,Hq,q_len/64,top_g] int32; lse
-[B,Hq,q_len] float32.  All contiguous, on the current GPU.
+[B,Hq,q_len] float32.  All contiguous, on the current GPU, except that K and
+V may also be pinned host tensors (``pin_memory=True``): HIP maps pinned host
+memory into the GPU's address space, and the kernels then fetch the rows they
+gather (the kept groups) across the host link.
 """
 from __future__ import annotations
 
@@ -114,15 +117,42 @@ def _elt_dtype(shape: HgaShape):
     return torch.bfloat16 if shape.dtype == HGA_DTYPE_BF16 else torch.float32
 
 
-def _ptr(t, name, dtype=None, size=None, nullable=False):
-    """Device pointer of a contiguous tensor after checking dtype and shape."""
+_hip = None
+
+
+def _hip_runtime():
+    """The HIP runtime torch has loaded (shared by soname with libhga.so)."""
+    global _hip
+    if _hip is None:
+        import torch  # noqa: F401  (loads the runtime)
+        _hip = ctypes.CDLL("libamdhip64.so.7")
+        _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                                 ctypes.c_uint]
+        _hip.hipHostGetDevicePointer.restype = ctypes.c_int
+    return _hip
+
+
+def _host_device_address(t, name):
+    """GPU address of a pinned host tensor; raises unless HIP maps it."""
+    if not t.is_pinned():
+        raise HGAError(f"{name} is a host tensor but not pinned (allocate it with pin_memory=True)")
+    dp = ctypes.c_void_p()
+    rc = _hip_runtime().hipHostGetDevicePointer(ctypes.byref(dp), ctypes.c_void_p(t.data_ptr()), 0)
+    if rc != 0 or not dp.value:
+        raise HGAError(f"{name}: HIP does not map this pinned host memory (hipError {rc})")
+    return dp.value
+
+
+def _ptr(t, name, dtype=None, size=None, nullable=False, host_ok=False):
+    """Device pointer of a contiguous tensor after checking dtype and shape.
+    With host_ok, a pinned host tensor is accepted and its GPU address used."""
     if t is None:
         if nullable:
             return None
         raise HGAError(f"{name} is required")
     if isinstance(t, int):
         return t
-    if not t.is_cuda:
+    if not t.is_cuda and not host_ok:
         raise HGAError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise HGAError(f"{name} must be contiguous")
@@ -130,6 +160,8 @@ def _ptr(t, name, dtype=None, size=None, nullable=False):
         raise HGAError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if size is not None and tuple(t.shape) != tuple(size):
         raise HGAError(f"{name} has shape {tuple(t.shape)}, expected {tuple(size)}")
+    if not t.is_cuda:
+        return _host_device_address(t, name)
     return t.data_ptr()
 
 
@@ -170,7 +202,7 @@ def hga_build_summaries(shape, K, chunk_mean, group_mean, chunk_begin=0, chunk_e
     if chunk_end is None:
         chunk_end = shape.kv_len // CHUNK
     _check(_load().hga_build_summaries(
-        ctypes.byref(shape), _ptr(K, "K", _elt_dtype(shape), sz["kv"]),
+        ctypes.byref(shape), _ptr(K, "K", _elt_dtype(shape), sz["kv"], host_ok=True),
         _ptr(chunk_mean, "chunk_mean", torch.float32, sz["cm"]),
         _ptr(group_mean, "group_mean", torch.float32, sz["gm"]),
         int(chunk_begin), int(chunk_end), _stream(stream)), "hga_build_summaries")
@@ -192,8 +224,8 @@ def hga_attend_fwd(shape, Q, K, V, group_idx, O, lse=None, stream=None):
     import torch
     sz, dt = _sizes(shape), _elt_dtype(shape)
     _check(_load().hga_attend_fwd(
-        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"]),
-        _ptr(V, "V", dt, sz["kv"]),
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"], host_ok=True),
+        _ptr(V, "V", dt, sz["kv"], host_ok=True),
         _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
         _ptr(O, "O", dt, sz["q"]), _ptr(lse, "lse", torch.float32, sz["lse"], nullable=True),
         _stream(stream)), "hga_attend_fwd")
@@ -217,8 +249,8 @@ def hga_attend_bwd(shape, Q, K, V, O, lse, dO, group_idx, dQ, dK, dV, workspace,
     sz, dt = _sizes(shape), _elt_dtype(shape)
     wp, wb = _ws(workspace)
     _check(_load().hga_attend_bwd(
-        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"]),
-        _ptr(V, "V", dt, sz["kv"]), _ptr(O, "O", dt, sz["q"]),
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"], host_ok=True),
+        _ptr(V, "V", dt, sz["kv"], host_ok=True), _ptr(O, "O", dt, sz["q"]),
         _ptr(lse, "lse", torch.float32, sz["lse"]), _ptr(dO, "dO", dt, sz["q"]),
         _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
         _ptr(dQ, "dQ", dt, sz["q"]), _ptr(dK, "dK", dt, sz["kv"]), _ptr(dV, "dV", dt, sz["kv"]),
@@ -230,8 +262,8 @@ def hga_attend_bwd_dq(shape, Q, K, V, O, lse, dO, group_idx, dQ, workspace, stre
     sz, dt = _sizes(shape), _elt_dtype(shape)
     wp, wb = _ws(workspace)
     _check(_load().hga_attend_bwd_dq(
-        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"]),
-        _ptr(V, "V", dt, sz["kv"]), _ptr(O, "O", dt, sz["q"]),
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"], host_ok=True),
+        _ptr(V, "V", dt, sz["kv"], host_ok=True), _ptr(O, "O", dt, sz["q"]),
         _ptr(lse, "lse", torch.float32, sz["lse"]), _ptr(dO, "dO", dt, sz["q"]),
         _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
         _ptr(dQ, "dQ", dt, sz["q"]), wp, wb, _stream(stream)), "hga_attend_bwd_dq")
@@ -242,8 +274,8 @@ def hga_attend_bwd_dkdv(shape, Q, K, V, lse, dO, group_idx, dK, dV, workspace, s
     sz, dt = _sizes(shape), _elt_dtype(shape)
     wp, wb = _ws(workspace)
     _check(_load().hga_attend_bwd_dkdv(
-        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"]),
-        _ptr(V, "V", dt, sz["kv"]), _ptr(lse, "lse", torch.float32, sz["lse"]),
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"], host_ok=True),
+        _ptr(V, "V", dt, sz["kv"], host_ok=True), _ptr(lse, "lse", torch.float32, sz["lse"]),
         _ptr(dO, "dO", dt, sz["q"]),
         _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
         _ptr(dK, "dK", dt, sz["kv"]), _ptr(dV, "dV", dt, sz["kv"]), wp, wb, _stream(stream)),
@@ -256,8 +288,8 @@ def hga_attend_bwd_dkdv_range(shape, Q, K, V, lse, dO, group_idx, chunk_begin, c
     sz, dt = _sizes(shape), _elt_dtype(shape)
     wp, wb = _ws(workspace)
     _check(_load().hga_attend_bwd_dkdv_range(
-        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"]),
-        _ptr(V, "V", dt, sz["kv"]), _ptr(lse, "lse", torch.float32, sz["lse"]),
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"], host_ok=True),
+        _ptr(V, "V", dt, sz["kv"], host_ok=True), _ptr(lse, "lse", torch.float32, sz["lse"]),
         _ptr(dO, "dO", dt, sz["q"]),
         _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
         int(chunk_begin), int(chunk_end),

@@ -24,6 +24,11 @@ Every step is a call of the C ABI; this module only sequences them and owns
 the buffers.  The caller writes a segment's keys and values into
 ``k_history[:, :, i*S:(i+1)*S]`` (and the same for ``v_history``) before
 calling ``step(i, ...)``.
+
+With ``kv_on_host=True`` the key/value history lives in pinned host memory
+(the page's RAM tier, same section): the summaries stay in GPU memory, and the
+kernels fetch only the rows they gather (the kept groups, the own chunk, the
+segment's keys for its dK/dV) across the host link.
 """
 from __future__ import annotations
 
@@ -46,7 +51,7 @@ class SegmentResult:
 class SegmentRunner:
     def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int,
                  seg_len: int, top_k: int, top_g: int, dtype: str = "bf16",
-                 softmax_scale: float = 0.0, device="cuda:0"):
+                 softmax_scale: float = 0.0, device="cuda:0", kv_on_host: bool = False):
         import torch
         if seg_len % CHUNK or seq_len % seg_len:
             raise ValueError("seg_len must be a multiple of 64 dividing seq_len")
@@ -59,8 +64,12 @@ class SegmentRunner:
         kv = (batch, n_kv_heads, seq_len, head_dim)
         q = (batch, n_q_heads, seg_len, head_dim)
         nblk = seg_len // 64
-        self.k_history = torch.zeros(kv, dtype=elt, device=device)
-        self.v_history = torch.zeros(kv, dtype=elt, device=device)
+        if kv_on_host:
+            self.k_history = torch.zeros(kv, dtype=elt, pin_memory=True)
+            self.v_history = torch.zeros(kv, dtype=elt, pin_memory=True)
+        else:
+            self.k_history = torch.zeros(kv, dtype=elt, device=device)
+            self.v_history = torch.zeros(kv, dtype=elt, device=device)
         self.chunk_mean = torch.zeros(batch, n_kv_heads, seq_len // 64, head_dim, dtype=f32,
                                       device=device)
         self.group_mean = torch.zeros(batch, n_kv_heads, seq_len // 8, head_dim, dtype=f32,
