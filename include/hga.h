@@ -26,7 +26,10 @@
  *
  * Conventions for every call:
  *   - all tensor pointers are DEVICE pointers to contiguous row-major buffers
- *     owned by the caller, 16-byte aligned; outputs must not alias inputs;
+ *     owned by the caller, 16-byte aligned; outputs must not alias inputs; K
+ *     and V may be the GPU address of pinned host memory (hipHostMalloc,
+ *     hipHostGetDevicePointer): the kernels then read the rows they gather
+ *     across the host link;
  *   - Q, O, dO, dQ are [B][Hq][q_len][D]; K, V, dK, dV are [B][Hkv][C][D]
  *     with C = kv_capacity (kv_len when 0): rows kv_len..C-1 of each
  *     (b, kv head) are not read, so a history that grows segment by segment
