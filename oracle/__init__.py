@@ -50,6 +50,8 @@ def _load():
         lib.hgao_attend_bwd.argtypes = ([i] * 9 + [ctypes.c_double, _dp, _dp, _dp, _ip, _dp,
                                                    _dp, _dp, _dp])
         lib.hgao_attended_pairs.argtypes = [i, i, i, i, i, i, _ip]
+        lib.hgao_decode.argtypes = ([i] * 9 + [ctypes.c_double, _dp, _dp, _dp, _dp, _dp, _ip, _ip,
+                                              _ip, _dp, _dp, _dp, _dp])
         lib.hgao_attended_pairs.restype = ctypes.c_longlong
         _lib = lib
     return _lib
@@ -110,6 +112,39 @@ def route(Q, chunk_mean, group_mean, Skv: int, top_k: int, top_g: int, C: int = 
     if want_scores:
         return ci, gi, cs, gs
     return ci, gi
+
+
+def decode(Q, K, V, chunk_mean, group_mean, top_k: int, top_g: int, scale: float = 0.0,
+           C: int = 64, G: int = 8, forced_chunk_idx=None, want_scores: bool = False):
+    """One query per (b, hq) at the last position of the L-token cache K, V.
+
+    Q [B,Hq,D]; K, V [B,Hkv,L,D]; chunk_mean [B,Hkv,L//C,D]; group_mean
+    [B,Hkv,(L//C)*(C//G),D].  Returns ``(chunk_idx, group_idx, O, lse)`` and,
+    with ``want_scores``, also ``(chunk_score, group_score)`` (NaN where no
+    candidate).
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    chunk_mean, group_mean = _f64(chunk_mean), _f64(group_mean)
+    B, Hq, D = Q.shape
+    Hkv, L = K.shape[1], K.shape[2]
+    nca = L // C
+    ci = np.empty((B, Hq, top_k), dtype=np.int32)
+    gi = np.empty((B, Hq, top_g), dtype=np.int32)
+    O = np.empty((B, Hq, D))
+    lse = np.empty((B, Hq))
+    cs = np.empty((B, Hq, nca)) if want_scores else None
+    gs = np.empty((B, Hq, nca * (C // G))) if want_scores else None
+    forced = None
+    if forced_chunk_idx is not None:
+        forced = np.ascontiguousarray(forced_chunk_idx, dtype=np.int32)
+        assert forced.shape == ci.shape
+    rc = _load().hgao_decode(B, Hq, Hkv, L, D, C, G, top_k, top_g, scale, _d(Q), _d(K), _d(V),
+                             _d(chunk_mean), _d(group_mean), _i(forced), _i(ci), _i(gi), _d(O),
+                             _d(lse), _d(cs), _d(gs))
+    _check(rc, "decode")
+    if want_scores:
+        return ci, gi, O, lse, cs, gs
+    return ci, gi, O, lse
 
 
 def attend_fwd(Q, K, V, group_idx, scale: float = 0.0, C: int = 64, G: int = 8):

@@ -34,7 +34,11 @@
  *  - order is (score descending, index ascending); kept indices are emitted in
  *    ascending order and padded with -1;
  *  - softmax scale 1/sqrt(D) unless given; lse in natural log;
- *  - the backward holds the routing fixed (no gradient through selection).
+ *  - the backward holds the routing fixed (no gradient through selection);
+ *  - decode (one new token at the end of an L-token cache) is the block form
+ *    with a block of one query: the routing query is that query, the
+ *    candidates are the complete chunks before its own chunk (L-1)/C, and the
+ *    own chunk is attended from its start up to the query.
  */
 #include <algorithm>
 #include <cmath>
@@ -343,6 +347,106 @@ int hgao_attend_bwd(int B, int Hq, int Hkv, int Sq, int Skv, int D, int C, int G
           }
         }
       }
+    }
+  return 0;
+}
+
+/* Decode: one new query per (b, hq), at the last position p = L - 1 of an
+ * L-token key/value cache (page section "What HGA does differently", applied
+ * to generation: the newest token routes over the resident chunk summaries and
+ * attends the exact tokens of its kept groups and of its own chunk).
+ * Reading: the routing query of a block that holds a single query is that
+ * query; the candidates are the complete chunks strictly before the query's
+ * own chunk cp = p / C; the own chunk is attended from its start up to p.
+ *   Q [B][Hq][D]; K, V [B][Hkv][L][D]; chunk_mean [B][Hkv][L/C][D];
+ *   group_mean [B][Hkv][(L/C)*(C/G)][D]; chunk_idx [B][Hq][top_k];
+ *   group_idx [B][Hq][top_g]; O [B][Hq][D]; lse [B][Hq];
+ *   chunk_score [B][Hq][L/C], group_score [B][Hq][(L/C)*(C/G)] (NaN where no
+ *   candidate), both nullable; forced_chunk_idx [B][Hq][top_k] nullable. */
+int hgao_decode(int B, int Hq, int Hkv, int L, int D, int C, int G, int top_k, int top_g,
+                double scale, const double* Q, const double* K, const double* V,
+                const double* chunk_mean, const double* group_mean,
+                const int32_t* forced_chunk_idx, int32_t* chunk_idx, int32_t* group_idx,
+                double* O, double* lse, double* chunk_score, double* group_score) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || C <= 0 || G <= 0 || L <= 0) return 2;
+  if (Hq % Hkv != 0 || C % G != 0 || top_k < 0 || top_g < 0) return 2;
+  if (!all_finite(Q, (long long)B * Hq * D)) return 4;
+  if (scale <= 0.0) scale = 1.0 / std::sqrt((double)D);
+  const int r = Hq / Hkv, gpc = C / G;
+  const int nca = L / C, nga = nca * gpc;   /* summary rows present */
+  const int p = L - 1, cp = p / C;          /* query position, its own chunk */
+  const double nan = std::nan("");
+  for (int b = 0; b < B; ++b)
+    for (int hq = 0; hq < Hq; ++hq) {
+      const int hkv = hq / r;
+      const long long row = (long long)b * Hq + hq;
+      const double* q = Q + row * D;
+
+      /* chunk stage */
+      if (chunk_score)
+        for (int c = 0; c < nca; ++c) chunk_score[row * nca + c] = nan;
+      std::vector<std::pair<double, int>> cand;
+      for (int c = 0; c < cp; ++c) {
+        double s = 0.0;
+        for (int d = 0; d < D; ++d) s += q[d] * chunk_mean[idx4(b, hkv, c, d, Hkv, nca, D)];
+        cand.push_back({s, c});
+        if (chunk_score) chunk_score[row * nca + c] = s;
+      }
+      std::vector<int> kept_chunks;
+      if (forced_chunk_idx) {
+        for (int i = 0; i < top_k; ++i) {
+          const int c = forced_chunk_idx[row * top_k + i];
+          if (c < 0) continue;
+          if (c >= cp) return 3;
+          kept_chunks.push_back(c);
+        }
+        std::sort(kept_chunks.begin(), kept_chunks.end());
+      } else {
+        kept_chunks = top_by_score(cand, top_k);
+      }
+      if (chunk_idx)
+        for (int i = 0; i < top_k; ++i)
+          chunk_idx[row * top_k + i] = i < (int)kept_chunks.size() ? kept_chunks[i] : -1;
+
+      /* group stage, joint over the kept chunks' groups */
+      if (group_score)
+        for (int g = 0; g < nga; ++g) group_score[row * nga + g] = nan;
+      std::vector<std::pair<double, int>> gcand;
+      for (int c : kept_chunks)
+        for (int t = 0; t < gpc; ++t) {
+          const int gam = c * gpc + t;
+          double s = 0.0;
+          for (int d = 0; d < D; ++d) s += q[d] * group_mean[idx4(b, hkv, gam, d, Hkv, nga, D)];
+          gcand.push_back({s, gam});
+          if (group_score) group_score[row * nga + gam] = s;
+        }
+      std::vector<int> kept_groups = top_by_score(gcand, top_g);
+      std::vector<int32_t> groups(top_g > 0 ? top_g : 1, -1);
+      for (int i = 0; i < top_g; ++i)
+        groups[i] = i < (int)kept_groups.size() ? kept_groups[i] : -1;
+      if (group_idx)
+        for (int i = 0; i < top_g; ++i) group_idx[row * top_g + i] = groups[i];
+
+      /* exact-token attention of the query over its key set */
+      std::vector<int> keys = key_set(groups.data(), top_g, G, C, cp, p);
+      std::vector<double> logit(keys.size());
+      double m = -INFINITY;
+      for (size_t a = 0; a < keys.size(); ++a) {
+        double s = 0.0;
+        for (int d = 0; d < D; ++d) s += q[d] * K[idx4(b, hkv, keys[a], d, Hkv, L, D)];
+        logit[a] = scale * s;
+        m = std::max(m, logit[a]);
+      }
+      double z = 0.0;
+      for (size_t a = 0; a < keys.size(); ++a) z += std::exp(logit[a] - m);
+      const double l = m + std::log(z);
+      for (int d = 0; d < D; ++d) {
+        double o = 0.0;
+        for (size_t a = 0; a < keys.size(); ++a)
+          o += std::exp(logit[a] - l) * V[idx4(b, hkv, keys[a], d, Hkv, L, D)];
+        O[row * D + d] = o;
+      }
+      if (lse) lse[row] = l;
     }
   return 0;
 }
