@@ -33,13 +33,15 @@ KERNEL_SOURCES = {
     "attend_fwd": ["attend_fwd.hip"],
     "attend_bwd_dq": ["attend_bwd.hip"],
     "attend_bwd_dkdv": ["attend_bwd.hip"],
+    "decode_route": ["route.hip"],
+    "decode_attend": ["decode.hip"],
 }
 
 
 def source_hash(phase: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "hierarchical_routed_sparse_amd", "csrc")
-    for f in KERNEL_SOURCES[phase] + ["hga_device.h"]:
+    for f in KERNEL_SOURCES[phase] + ["hga_device.h", "../build_lib.py"]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -59,7 +61,11 @@ def parse():
                     help="segment-wise mode: the 16384-token sequence as 8 segments of 2048, "
                          "each forward + backward with the history detached")
     ap.add_argument("--host-kv", action="store_true",
-                    help="with --segments: keep the key/value history in pinned host memory")
+                    help="with --segments or --decode: keep the keys and values in pinned "
+                         "host memory")
+    ap.add_argument("--decode", action="store_true",
+                    help="decode mode: one new token per sequence over a 16,424-token cache, "
+                         "batch 16 (routing + attention per step)")
     return ap.parse_args()
 
 
@@ -220,6 +226,157 @@ def segments_main(args):
     print(json.dumps(out))
 
 
+def decode_work(w, kept_groups: int) -> dict:
+    """Per-launch algorithmic bytes of the two decode kernels.  Routing: the
+    queries, the chunk summaries before the own chunk (read once for the query
+    heads of a kv head), the group summaries of every row's kept chunks, the
+    indices written.  Attention: per row the query, its group indices, the key
+    and value rows of its kept groups and of its own chunk up to the token, the
+    output row and lse."""
+    B, Hq, Hkv, D, L = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.kv_len
+    p = L - 1
+    cp = p // 64
+    kk = min(w.top_k, cp)
+    rows = B * Hq
+    route = rows * D * 2 + B * Hkv * cp * D * 4 + rows * kk * 8 * D * 4 + rows * (w.top_k + w.top_g) * 4
+    own = p - 64 * cp + 1
+    attend = rows * (D * 2 + D * 2 + 4) + kept_groups * 4 + (kept_groups * 8 + rows * own) * D * 2 * 2
+    return {"decode_route": route, "decode_attend": attend}
+
+
+def cpu_baseline_decode(w, x, cm, gm, budget_s: float = 12.0):
+    """The CPU oracle's decode (routing and attention of every head in fp64,
+    summaries given), single thread, over the batch's sequences one after
+    another, repeated until `budget_s` seconds of work are done."""
+    import oracle
+    from hierarchical_routed_sparse_amd import synthetic as syn
+    oracle.build(force=False)
+    seqs = []
+    for b in range(w.batch):
+        seqs.append((syn.to_f64(x["Q"][b:b + 1, :, 0], w.dtype), syn.to_f64(x["K"][b:b + 1], w.dtype),
+                     syn.to_f64(x["V"][b:b + 1], w.dtype), cm[b:b + 1], gm[b:b + 1]))
+        if b >= 3:
+            break                      # conversion bounded: four sequences are cycled
+    done, dt = 0, 0.0
+    while dt < budget_s:
+        Q, K, V, c, g = seqs[done % len(seqs)]
+        t0 = time.perf_counter()
+        oracle.decode(Q, K, V, c, g, w.top_k, w.top_g)
+        dt += time.perf_counter() - t0
+        done += 1
+    return {
+        "value": done / dt,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{done} single-sequence decode steps (all {w.n_q_heads} query heads: routing "
+                   f"over the resident summaries and attention, fp64) cycling over "
+                   f"{len(seqs)} of the {w.batch} sequences, {dt:.1f} s single-threaded"),
+    }
+
+
+def decode_main(args):
+    """Decode step of one layer: one new token for each of 16 sequences at
+    position 16423 of a 16,424-token cache (capacity 16,448); summaries of the
+    256 complete chunks resident (a decoder appends one chunk's summary every
+    64 tokens, outside this step).  Step = routing + attention, timed per kernel
+    with HIP events on the launch stream."""
+    import numpy as np
+    import torch
+    import hierarchical_routed_sparse_amd as hga
+    from hierarchical_routed_sparse_amd import synthetic as syn
+
+    w = syn.WORKLOADS["decode_b16_16k"]
+    x = syn.make_inputs(w)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    B, Hq, Hkv, D, L = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.kv_len
+    cap = -(-L // 64) * 64
+    s = hga.make_shape(B, Hq, Hkv, D, 1, L, w.top_k, w.top_g, dtype=w.dtype, kv_capacity=cap)
+    edt = torch.bfloat16
+    K = torch.zeros(B, Hkv, cap, D, dtype=edt, device=dev)
+    V = torch.zeros(B, Hkv, cap, D, dtype=edt, device=dev)
+    K[:, :, :L] = syn.to_torch(x["K"], w.dtype, dev)
+    V[:, :, :L] = syn.to_torch(x["V"], w.dtype, dev)
+    Q = syn.to_torch(x["Q"], w.dtype, dev)[:, :, 0].contiguous()
+    cm = torch.zeros(B, Hkv, cap // 64, D, device=dev)
+    gm = torch.zeros(B, Hkv, cap // 8, D, device=dev)
+    hga.hga_build_summaries(s, K, cm, gm, 0, L // 64)
+    if args.host_kv:
+        torch.cuda.synchronize()
+        Kh = torch.empty(K.shape, dtype=edt, pin_memory=True)
+        Vh = torch.empty(V.shape, dtype=edt, pin_memory=True)
+        Kh.copy_(K)
+        Vh.copy_(V)
+        K, V = Kh, Vh
+    ci = torch.empty(B, Hq, w.top_k, dtype=torch.int32, device=dev)
+    gi = torch.empty(B, Hq, w.top_g, dtype=torch.int32, device=dev)
+    O = torch.empty(B, Hq, D, dtype=edt, device=dev)
+    lse = torch.empty(B, Hq, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        hga.hga_decode_route(s, Q, cm, gm, ci, gi, stream=stream)
+        if ev: ev[1].record(stream)
+        hga.hga_decode_attend(s, Q, K, V, gi, O, lse, stream=stream)
+        if ev: ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    phases = ["decode_route", "decode_attend"]
+    phase_ms = {p: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+                for i, p in enumerate(phases)}
+    kept = int((gi >= 0).sum().item())
+    work = decode_work(w, kept)
+    rep = {}
+    for p in phases:
+        ach = work[p] / (phase_ms[p] * 1e-3) / 1e9
+        rep[p] = {"us": round(phase_ms[p] * 1e3, 2), "bound": "hbm",
+                  "algorithmic_bytes": work[p], "achieved_GBs": round(ach, 1),
+                  "frac": round(ach / PEAK_HBM_GBS, 4)}
+    dom = "decode_attend"
+    ach = work[dom] / (phase_ms[dom] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": ach / PEAK_HBM_GBS, "traffic": None if args.host_kv else load_traffic(dom),
+            "kernel": dom, "algorithmic_per_launch": work[dom]}
+    base = None
+    if not args.no_cpu_baseline:
+        base = cpu_baseline_decode(w, x, cm.cpu().numpy().astype(np.float64),
+                                   gm.cpu().numpy().astype(np.float64))
+    out = {
+        "metric": "HGA decode tokens/sec at 16K ctx (one new token per sequence, batch 16"
+                  + (", K/V in pinned host memory" if args.host_kv else "") + "), 1 MI355X",
+        "value": B / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded clustered keys, N(0,1)/sqrt(128) queries and values)",
+        "config": {"workload": f"{w.name}: decode at position {L - 1}, cache capacity {cap}",
+                   "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "kv_len": L,
+                   "chunk": 64, "group": 8, "top_k": w.top_k, "top_g": w.top_g,
+                   "kept_groups": kept},
+        "roofline": roof,
+        "phases": rep,
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -230,6 +387,9 @@ def main():
 
     if args.segments:
         segments_main(args)
+        return
+    if args.decode:
+        decode_main(args)
         return
 
     import torch

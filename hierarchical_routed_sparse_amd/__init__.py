@@ -6,14 +6,16 @@ every step of the method runs in the library's HIP kernels.  Torch is used for
 device memory and streams.  If ``libhga.so`` has not been built, the first call
 raises ``HGAError``: there is no fallback implementation.
 
-Tensors: Q, O, dO, dQ [B,Hq,q_len,D]; K, V, dK, dV [B,Hkv,C,D] of the
+Tensors (block shapes): Q, O, dO, dQ [B,Hq,q_len,D]; K, V, dK, dV [B,Hkv,C,D] of the
 shape's dtype (torch.bfloat16 or torch.float32), C = kv_capacity (kv_len when
 0); chunk_mean [B,Hkv,C/64,D] and group_mean [B,Hkv,C/8,D] float32; chunk_idx
 [B,Hq,q_len/64,top_k] and group_idx [B,Hq,q_len/64,top_g] int32; lse
 [B,Hq,q_len] float32.  All contiguous, on the current GPU, except that K and
 V may also be pinned host tensors (``pin_memory=True``): HIP maps pinned host
 memory into the GPU's address space, and the kernels then fetch the rows they
-gather (the kept groups) across the host link.
+gather (the kept groups) across the host link.  A decode shape (q_len == 1,
+``hga_decode``) takes Q and O [B,Hq,D], chunk_idx [B,Hq,top_k], group_idx
+[B,Hq,top_g] and lse [B,Hq].
 """
 from __future__ import annotations
 
@@ -24,7 +26,8 @@ __all__ = [
     "HGAError", "HgaShape", "make_shape", "lib_path", "hga_abi_version", "hga_validate_shape",
     "hga_build_summaries", "hga_route", "hga_attend_fwd", "hga_attend_bwd_workspace",
     "hga_attend_bwd", "hga_attend_bwd_dq", "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range",
-    "forward", "backward",
+    "hga_validate_decode_shape", "hga_decode", "hga_decode_route", "hga_decode_attend",
+    "forward", "backward", "decode",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -90,7 +93,12 @@ def _load():
     lib.hga_attend_bwd_dq.argtypes = [_SP] + [_vp] * 9 + [sz, _vp]
     lib.hga_attend_bwd_dkdv.argtypes = [_SP] + [_vp] * 9 + [sz, _vp]
     lib.hga_attend_bwd_dkdv_range.argtypes = [_SP] + [_vp] * 6 + [i32, i32] + [_vp] * 3 + [sz, _vp]
-    for name in ("hga_validate_shape", "hga_build_summaries", "hga_route", "hga_attend_fwd",
+    lib.hga_validate_decode_shape.argtypes = [_SP]
+    lib.hga_decode.argtypes = [_SP] + [_vp] * 10
+    lib.hga_decode_route.argtypes = [_SP] + [_vp] * 6
+    lib.hga_decode_attend.argtypes = [_SP] + [_vp] * 7
+    for name in ("hga_validate_shape", "hga_validate_decode_shape", "hga_decode",
+                 "hga_decode_route", "hga_decode_attend", "hga_build_summaries", "hga_route", "hga_attend_fwd",
                  "hga_attend_bwd_workspace", "hga_attend_bwd", "hga_attend_bwd_dq",
                  "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range"):
         getattr(lib, name).restype = ctypes.c_int
@@ -171,8 +179,18 @@ def capacity(s: HgaShape) -> int:
 
 
 def _sizes(s: HgaShape):
-    nblk = s.q_len // QBLOCK
     cap = capacity(s)
+    if s.q_len == 1:   # decode shape
+        return dict(
+            q=(s.batch, s.n_q_heads, s.head_dim),
+            kv=(s.batch, s.n_kv_heads, cap, s.head_dim),
+            cm=(s.batch, s.n_kv_heads, cap // CHUNK, s.head_dim),
+            gm=(s.batch, s.n_kv_heads, cap // GROUP, s.head_dim),
+            ci=(s.batch, s.n_q_heads, s.top_k),
+            gi=(s.batch, s.n_q_heads, s.top_g),
+            lse=(s.batch, s.n_q_heads),
+        )
+    nblk = s.q_len // QBLOCK
     return dict(
         q=(s.batch, s.n_q_heads, s.q_len, s.head_dim),
         kv=(s.batch, s.n_kv_heads, cap, s.head_dim),
@@ -193,6 +211,11 @@ def hga_abi_version() -> int:
 def hga_validate_shape(shape: HgaShape) -> int:
     """Returns the status code (0 = valid); host only."""
     return _load().hga_validate_shape(ctypes.byref(shape))
+
+
+def hga_validate_decode_shape(shape: HgaShape) -> int:
+    """Returns the status code (0 = valid) of a decode shape; host only."""
+    return _load().hga_validate_decode_shape(ctypes.byref(shape))
 
 
 def hga_build_summaries(shape, K, chunk_mean, group_mean, chunk_begin=0, chunk_end=None,
@@ -297,6 +320,50 @@ def hga_attend_bwd_dkdv_range(shape, Q, K, V, lse, dO, group_idx, chunk_begin, c
         "hga_attend_bwd_dkdv_range")
 
 
+def hga_decode(shape, Q, K, V, chunk_mean, group_mean, chunk_idx, group_idx, O, lse=None,
+               stream=None):
+    import torch
+    sz, dt = _decode_sizes(shape)
+    _check(_load().hga_decode(
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"], host_ok=True),
+        _ptr(V, "V", dt, sz["kv"], host_ok=True),
+        _ptr(chunk_mean, "chunk_mean", torch.float32, sz["cm"], nullable=True),
+        _ptr(group_mean, "group_mean", torch.float32, sz["gm"], nullable=True),
+        _ptr(chunk_idx, "chunk_idx", torch.int32, sz["ci"], nullable=True),
+        _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        _ptr(O, "O", dt, sz["q"]), _ptr(lse, "lse", torch.float32, sz["lse"], nullable=True),
+        _stream(stream)), "hga_decode")
+
+
+def _decode_sizes(shape):
+    if shape.q_len != 1:
+        raise HGAError("decode calls take a decode shape (q_len == 1)")
+    return _sizes(shape), _elt_dtype(shape)
+
+
+def hga_decode_route(shape, Q, chunk_mean, group_mean, chunk_idx, group_idx, stream=None):
+    import torch
+    sz, dt = _decode_sizes(shape)
+    _check(_load().hga_decode_route(
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]),
+        _ptr(chunk_mean, "chunk_mean", torch.float32, sz["cm"], nullable=True),
+        _ptr(group_mean, "group_mean", torch.float32, sz["gm"], nullable=True),
+        _ptr(chunk_idx, "chunk_idx", torch.int32, sz["ci"], nullable=True),
+        _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        _stream(stream)), "hga_decode_route")
+
+
+def hga_decode_attend(shape, Q, K, V, group_idx, O, lse=None, stream=None):
+    import torch
+    sz, dt = _decode_sizes(shape)
+    _check(_load().hga_decode_attend(
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"], host_ok=True),
+        _ptr(V, "V", dt, sz["kv"], host_ok=True),
+        _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        _ptr(O, "O", dt, sz["q"]), _ptr(lse, "lse", torch.float32, sz["lse"], nullable=True),
+        _stream(stream)), "hga_decode_attend")
+
+
 # ------------------------------------------------------------------ compositions
 
 def forward(shape, Q, K, V, stream=None):
@@ -331,3 +398,21 @@ def backward(shape, Q, K, V, O, lse, dO, group_idx, stream=None):
     ws = torch.empty(hga_attend_bwd_workspace(shape), dtype=torch.uint8, device=dev)
     hga_attend_bwd(shape, Q, K, V, O, lse, dO, group_idx, dQ, dK, dV, ws, stream=stream)
     return dQ, dK, dV
+
+
+def decode(shape, Q, K, V, chunk_mean, group_mean, stream=None):
+    """One decode step with freshly allocated outputs (the summaries of every
+    complete chunk before the token's own chunk already built).
+    Returns dict(chunk_idx, group_idx, O, lse)."""
+    import torch
+    sz = _sizes(shape)
+    dev = Q.device
+    out = dict(
+        chunk_idx=torch.empty(sz["ci"], dtype=torch.int32, device=dev),
+        group_idx=torch.empty(sz["gi"], dtype=torch.int32, device=dev),
+        O=torch.empty(sz["q"], dtype=_elt_dtype(shape), device=dev),
+        lse=torch.empty(sz["lse"], dtype=torch.float32, device=dev),
+    )
+    hga_decode(shape, Q, K, V, chunk_mean, group_mean, out["chunk_idx"], out["group_idx"],
+               out["O"], out["lse"], stream=stream)
+    return out

@@ -17,14 +17,18 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhga.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["hga_api.hip", "summaries.hip", "route.hip", "attend_fwd.hip", "attend_bwd.hip"]
+SOURCES = ["hga_api.hip", "summaries.hip", "route.hip", "attend_fwd.hip", "attend_bwd.hip",
+           "decode.hip"]
 HEADERS = ["hga_device.h", "hga_kernels.h", "bwd_common.h"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-fno-gpu-rdc", "-ffp-contract=fast",
-    # inputs are finite by contract: no NaN canonicalisation around min/max
-    "-mno-amdgpu-ieee", "-fno-honor-nans",
+    # inputs are finite by contract: no NaN canonicalisation around min/max.
+    # (-mno-amdgpu-ieee is NOT used: it makes the kernels' attributes differ
+    # from the device library's, which then is not inlined: every threadIdx /
+    # blockIdx read becomes a call and every index derived from it divergent.)
+    "-fno-honor-nans",
     # MFMA accumulators in VGPRs (no AGPR round trips to rescale or read them)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     # packed fp32 instructions stay off: hipcc emits no v_pk_*_f32

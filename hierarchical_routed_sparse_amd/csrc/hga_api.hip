@@ -21,7 +21,7 @@ hga::Dims dims_of(const hga_shape* s) {
   d.top_k = s->top_k;
   d.top_g = s->top_g;
   d.q0 = s->kv_len - s->q_len;
-  d.nblk = s->q_len / HGA_QBLOCK;
+  d.nblk = s->q_len == 1 ? 1 : s->q_len / HGA_QBLOCK;
   d.scale = s->softmax_scale > 0.f ? s->softmax_scale : 1.0f / sqrtf((float)s->head_dim);
   d.bf16 = s->dtype == HGA_DTYPE_BF16;
   return d;
@@ -41,6 +41,21 @@ size_t cmask_bytes(const hga_shape* s) {
                   (s->kv_len / HGA_CHUNK));
 }
 size_t workspace_bytes(const hga_shape* s) { return delta_bytes(s) + cmask_bytes(s); }
+
+// Checks shared by block and decode shapes (everything but q_len, kv_len and
+// kv_capacity).
+hga_status validate_common(const hga_shape* s) {
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1) return HGA_ERR_SHAPE;
+  if (s->n_q_heads % s->n_kv_heads != 0) return HGA_ERR_SHAPE;
+  if (s->top_k < 0 || s->top_k > HGA_MAX_TOP_K) return HGA_ERR_SHAPE;
+  if (s->top_g < 0 || s->top_g > HGA_MAX_TOP_G) return HGA_ERR_SHAPE;
+  // NaN or infinite scale (checked on the bit pattern: the library is built
+  // with -fno-honor-nans, under which x != x may be folded away)
+  uint32_t sbits;
+  memcpy(&sbits, &s->softmax_scale, sizeof(sbits));
+  if ((sbits & 0x7F800000u) == 0x7F800000u) return HGA_ERR_SHAPE;
+  return HGA_OK;
+}
 
 }  // namespace
 
@@ -62,21 +77,14 @@ const char* hga_status_str(hga_status s) {
 
 hga_status hga_validate_shape(const hga_shape* s) {
   if (!s) return HGA_ERR_NULL;
-  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1) return HGA_ERR_SHAPE;
-  if (s->n_q_heads % s->n_kv_heads != 0) return HGA_ERR_SHAPE;
+  hga_status st = validate_common(s);
+  if (st != HGA_OK) return st;
   if (s->q_len < HGA_QBLOCK || s->q_len % HGA_QBLOCK != 0) return HGA_ERR_SHAPE;
   if (s->kv_len % HGA_CHUNK != 0 || s->kv_len < s->q_len || s->kv_len > HGA_MAX_KV_LEN)
     return HGA_ERR_SHAPE;
   if (s->kv_capacity != 0 && (s->kv_capacity < s->kv_len || s->kv_capacity % HGA_CHUNK != 0 ||
                               s->kv_capacity > HGA_MAX_KV_LEN))
     return HGA_ERR_SHAPE;
-  if (s->top_k < 0 || s->top_k > HGA_MAX_TOP_K) return HGA_ERR_SHAPE;
-  if (s->top_g < 0 || s->top_g > HGA_MAX_TOP_G) return HGA_ERR_SHAPE;
-  // NaN or infinite scale (checked on the bit pattern: the library is built
-  // with -fno-honor-nans, under which x != x may be folded away)
-  uint32_t sbits;
-  memcpy(&sbits, &s->softmax_scale, sizeof(sbits));
-  if ((sbits & 0x7F800000u) == 0x7F800000u) return HGA_ERR_SHAPE;
   if (s->head_dim != 64 && s->head_dim != 128) return HGA_ERR_UNSUPPORTED;
   if (s->dtype != HGA_DTYPE_BF16 && s->dtype != HGA_DTYPE_FP32) return HGA_ERR_UNSUPPORTED;
   // launch sizes must fit a 32-bit grid
@@ -90,10 +98,28 @@ hga_status hga_validate_shape(const hga_shape* s) {
   return HGA_OK;
 }
 
+hga_status hga_validate_decode_shape(const hga_shape* s) {
+  if (!s) return HGA_ERR_NULL;
+  hga_status st = validate_common(s);
+  if (st != HGA_OK) return st;
+  if (s->q_len != 1 || s->kv_len < 1 || s->kv_len > HGA_MAX_KV_LEN) return HGA_ERR_SHAPE;
+  const long long cap = s->kv_capacity > 0 ? s->kv_capacity : s->kv_len;
+  if (s->kv_capacity < 0 || cap < s->kv_len || cap % HGA_CHUNK != 0 || cap > HGA_MAX_KV_LEN)
+    return HGA_ERR_SHAPE;
+  if (s->head_dim != 64 && s->head_dim != 128) return HGA_ERR_UNSUPPORTED;
+  if (s->dtype != HGA_DTYPE_BF16 && s->dtype != HGA_DTYPE_FP32) return HGA_ERR_UNSUPPORTED;
+  // one workgroup per (b, query head); summaries rows as for block shapes
+  if ((long long)s->batch * s->n_q_heads > (1LL << 30) ||
+      (long long)s->batch * s->n_kv_heads * (cap / HGA_CHUNK) > (1LL << 30))
+    return HGA_ERR_SHAPE;
+  return HGA_OK;
+}
+
 hga_status hga_build_summaries(const hga_shape* shape, const void* K, float* chunk_mean,
                                float* group_mean, int32_t chunk_begin, int32_t chunk_end,
                                void* stream) {
-  hga_status st = hga_validate_shape(shape);
+  hga_status st = shape && shape->q_len == 1 ? hga_validate_decode_shape(shape)
+                                             : hga_validate_shape(shape);
   if (st != HGA_OK) return st;
   if (!K || !chunk_mean || !group_mean) return HGA_ERR_NULL;
   if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > shape->kv_len / HGA_CHUNK)
@@ -191,6 +217,46 @@ hga_status hga_attend_bwd(const hga_shape* shape, const void* Q, const void* K, 
   if (st != HGA_OK) return st;
   return hga_attend_bwd_dkdv(shape, Q, K, V, lse, dO, group_idx, dK, dV, workspace,
                              workspace_bytes, stream);
+}
+
+hga_status hga_decode_route(const hga_shape* shape, const void* Q, const float* chunk_mean,
+                            const float* group_mean, int32_t* chunk_idx, int32_t* group_idx,
+                            void* stream) {
+  hga_status st = hga_validate_decode_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!Q) return HGA_ERR_NULL;
+  if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
+  // summaries are read only when the token has candidate chunks
+  const bool candidates = shape->kv_len > HGA_CHUNK && (shape->top_k > 0 || shape->top_g > 0);
+  if (candidates && (!chunk_mean || (shape->top_g > 0 && !group_mean))) return HGA_ERR_NULL;
+  if (shape->top_k == 0 && shape->top_g == 0) return HGA_OK;
+  // launched also without candidates: it then writes the -1 padding
+  return from_hip(hga::launch_route(dims_of(shape), Q, chunk_mean, group_mean,
+                                    shape->top_k > 0 ? chunk_idx : nullptr,
+                                    shape->top_g > 0 ? group_idx : nullptr,
+                                    (hipStream_t)stream));
+}
+
+hga_status hga_decode_attend(const hga_shape* shape, const void* Q, const void* K, const void* V,
+                             const int32_t* group_idx, void* O, float* lse, void* stream) {
+  hga_status st = hga_validate_decode_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!Q || !K || !V || !O) return HGA_ERR_NULL;
+  if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
+  return from_hip(hga::launch_decode_attend(dims_of(shape), Q, K, V, group_idx, O, lse,
+                                            (hipStream_t)stream));
+}
+
+hga_status hga_decode(const hga_shape* shape, const void* Q, const void* K, const void* V,
+                      const float* chunk_mean, const float* group_mean, int32_t* chunk_idx,
+                      int32_t* group_idx, void* O, float* lse, void* stream) {
+  // every argument check of both halves before anything is launched
+  hga_status st = hga_validate_decode_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!K || !V || !O) return HGA_ERR_NULL;
+  st = hga_decode_route(shape, Q, chunk_mean, group_mean, chunk_idx, group_idx, stream);
+  if (st != HGA_OK) return st;
+  return hga_decode_attend(shape, Q, K, V, group_idx, O, lse, stream);
 }
 
 }  // extern "C"

@@ -11,7 +11,7 @@ struct Dims {
   int B, Hq, Hkv, D, Sq, Skv, top_k, top_g;
   int Scap;    // rows allocated per (b, kv head) in K, V, dK, dV (>= Skv)
   int q0;      // Skv - Sq: absolute position of the first query
-  int nblk;    // Sq / 64
+  int nblk;    // Sq / 64 (1 for a decode shape, whose one query is a block)
   float scale; // softmax scale
   bool bf16;
 };
@@ -35,5 +35,9 @@ hipError_t launch_attend_bwd_dkdv(const Dims& d, const void* Q, const void* K, c
                                   const float* lse, const void* dO, const int32_t* group_idx,
                                   const float* delta, const uint8_t* cmask, void* dK, void* dV,
                                   int chunk_begin, int chunk_end, hipStream_t s);
+
+// Decode attention (one query per (b, hq) at position Skv - 1; d.Sq == 1).
+hipError_t launch_decode_attend(const Dims& d, const void* Q, const void* K, const void* V,
+                                const int32_t* group_idx, void* O, float* lse, hipStream_t s);
 
 }  // namespace hga

@@ -11,6 +11,7 @@
 // head); those rows share the candidate chunks and the summaries.
 //   1. each wavefront computes one row's block query (mean of its 64 query
 //      rows: 16 independent 16-byte loads per lane, then a cross-lane sum);
+//      in decode (a block of one query, QB = 1) the block query is the query;
 //   2. chunk scores: eight lanes share one summary row (whole 128-byte lines
 //      per load), each summary is loaded once for all rows of the set, and the
 //      block queries stay in registers (fp32, fixed summation order); scores
@@ -118,7 +119,7 @@ __device__ __forceinline__ float sum8(float v) {
   return v;
 }
 
-template <typename T, int D, int NSC, int NSG>
+template <typename T, int D, int QB, int NSC, int NSG>
 __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
   constexpr int kGroupSlots = NSG;   // group candidates per row: up to 64 * NSG
   constexpr int kMaxChunks = 64 * NSC;
@@ -144,7 +145,16 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
 
   // 1. block query of row wv (head hkv*r + h0 + wv): lane (o = l%16, rg = l/16)
   //    sums rows 16rg..16rg+15 of columns 8o..8o+7
-  if (wv < nrows) {
+  if constexpr (QB == 1) {
+    if (wv < nrows && lane < D / 8) {
+      const int hq = hkv * r + h0 + wv;
+      Frag<T> x;
+      load_frag(x, reinterpret_cast<const T*>(p.Q) + ((long long)b * p.Hq + hq) * D + 8 * lane);
+      const T* v = reinterpret_cast<const T*>(&x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_qbar[wv][8 * lane + e] = to_f32(v[e]);
+    }
+  } else if (wv < nrows) {
     const int hq = hkv * r + h0 + wv;
     const T* Qb = reinterpret_cast<const T*>(p.Q) + (((long long)b * p.Hq + hq) * p.Sq + (long long)blk * kChunk) * D;
     constexpr int kOct = D / 8;                 // 8-element columns
@@ -288,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
   }
 }
 
-template <typename T, int D, int NSC, int NSG>
+template <typename T, int D, int QB, int NSC, int NSG>
 hipError_t run(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
                int32_t* gi, hipStream_t s) {
   RouteP p;
@@ -298,27 +308,34 @@ hipError_t run(const Dims& d, const void* Q, const float* cm, const float* gm, i
   const int r = d.Hq / d.Hkv;
   p.nsets = (r + kRowsPerWG - 1) / kRowsPerWG;
   p.nwork = d.B * d.Hkv * d.nblk * p.nsets;
-  route_kernel<T, D, NSC, NSG><<<p.nwork, kThreads, 0, s>>>(p);
+  route_kernel<T, D, QB, NSC, NSG><<<p.nwork, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
-template <typename T, int D, int NSC>
+template <typename T, int D, int QB, int NSC>
 hipError_t run_g(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
                  int32_t* gi, hipStream_t s) {
   // 8 * top_k group candidates per row at most
-  if (d.top_k <= 8) return run<T, D, NSC, 1>(d, Q, cm, gm, ci, gi, s);
-  if (d.top_k <= 16) return run<T, D, NSC, 2>(d, Q, cm, gm, ci, gi, s);
-  if (d.top_k <= 32) return run<T, D, NSC, 4>(d, Q, cm, gm, ci, gi, s);
-  return run<T, D, NSC, 8>(d, Q, cm, gm, ci, gi, s);
+  if (d.top_k <= 8) return run<T, D, QB, NSC, 1>(d, Q, cm, gm, ci, gi, s);
+  if (d.top_k <= 16) return run<T, D, QB, NSC, 2>(d, Q, cm, gm, ci, gi, s);
+  if (d.top_k <= 32) return run<T, D, QB, NSC, 4>(d, Q, cm, gm, ci, gi, s);
+  return run<T, D, QB, NSC, 8>(d, Q, cm, gm, ci, gi, s);
+}
+
+template <typename T, int D, int QB>
+hipError_t run_c(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
+                 int32_t* gi, hipStream_t s) {
+  const int max_cand = (d.Skv - 1) / kChunk;   // chunks before the last query's own chunk
+  if (max_cand <= 256) return run_g<T, D, QB, 4>(d, Q, cm, gm, ci, gi, s);
+  if (max_cand <= 1024) return run_g<T, D, QB, 16>(d, Q, cm, gm, ci, gi, s);
+  return run_g<T, D, QB, 32>(d, Q, cm, gm, ci, gi, s);
 }
 
 template <typename T, int D>
 hipError_t run_d(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
                  int32_t* gi, hipStream_t s) {
-  const int max_cand = d.Skv / kChunk - 1;   // chunks before the last block's own chunk
-  if (max_cand <= 256) return run_g<T, D, 4>(d, Q, cm, gm, ci, gi, s);
-  if (max_cand <= 1024) return run_g<T, D, 16>(d, Q, cm, gm, ci, gi, s);
-  return run_g<T, D, 32>(d, Q, cm, gm, ci, gi, s);
+  return d.Sq == 1 ? run_c<T, D, 1>(d, Q, cm, gm, ci, gi, s)
+                   : run_c<T, D, kChunk>(d, Q, cm, gm, ci, gi, s);
 }
 
 }  // namespace

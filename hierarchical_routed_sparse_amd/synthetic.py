@@ -31,6 +31,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
 
 import numpy as np
 
@@ -67,26 +68,54 @@ def uniforms(state: int, first: int, count: int) -> np.ndarray:
     return (z >> np.uint64(11)).astype(np.float64) * (1.0 / 9007199254740992.0)
 
 
+def _normals_block(state: int, out: np.ndarray, pos: int, n: int) -> None:
+    u = uniforms(state, pos, n)
+    r = np.sqrt(-2.0 * np.log1p(-u[0::2]))
+    th = (2.0 * math.pi) * u[1::2]
+    out[pos:pos + n:2] = r * np.cos(th)
+    out[pos + 1:pos + n:2] = r * np.sin(th)
+
+
 def normals(state: int, count: int) -> np.ndarray:
-    """count standard normals (count rounded up to even internally)."""
+    """count standard normals (count rounded up to even internally).  Blocks of
+    the stream are independent (counter based), so large draws are split over
+    threads (numpy releases the GIL inside each block's array operations); the
+    values do not depend on the thread count."""
     out = np.empty(count + (count & 1), dtype=np.float64)
-    pos = 0
-    while pos < out.size:
-        n = min(_BLOCK, out.size - pos)
-        u = uniforms(state, pos, n)
-        r = np.sqrt(-2.0 * np.log1p(-u[0::2]))
-        th = (2.0 * math.pi) * u[1::2]
-        out[pos:pos + n:2] = r * np.cos(th)
-        out[pos + 1:pos + n:2] = r * np.sin(th)
-        pos += n
+    starts = list(range(0, out.size, _BLOCK))
+    work = [(p, min(_BLOCK, out.size - p)) for p in starts]
+    if len(work) <= 2:
+        for p, n in work:
+            _normals_block(state, out, p, n)
+    else:
+        import concurrent.futures as cf
+        threads = max(1, min(16, os.cpu_count() or 1, len(work)))
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(lambda pn: _normals_block(state, out, *pn), work))
     return out[:count]
 
 
-def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """float32 -> bfloat16 bit patterns (uint16), round to nearest even."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+def _bf16_block(src: np.ndarray, dst: np.ndarray) -> None:
+    b = src.view(np.uint32).astype(np.uint64)
     b = b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))
-    return (b >> np.uint64(16)).astype(np.uint16)
+    dst[...] = (b >> np.uint64(16)).astype(np.uint16)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even
+    (elementwise; large arrays are converted in blocks over threads)."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    flat = x32.reshape(-1)
+    out = np.empty(flat.size, dtype=np.uint16)
+    spans = [(p, min(p + _BLOCK, flat.size)) for p in range(0, flat.size, _BLOCK)]
+    if len(spans) <= 2:
+        for a, b in spans:
+            _bf16_block(flat[a:b], out[a:b])
+    else:
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as ex:
+            list(ex.map(lambda ab: _bf16_block(flat[ab[0]:ab[1]], out[ab[0]:ab[1]]), spans))
+    return out.reshape(x32.shape)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -136,6 +165,11 @@ WORKLOADS = {
                  1 / math.sqrt(128), backward=True,
                  description="bf16 causal self-attention, batch 2, 32q/8kv, D128, 4K tokens, "
                              "k8 g32, forward + backward"),
+        Workload("decode_b16_16k", 16, 32, 8, 128, 1, 16424, 16, 64, "bf16", 5,
+                 1 / math.sqrt(128),
+                 description="bf16 decode: one new token per sequence at position 16423 of "
+                             "a 16424-token cache (40 tokens into its own chunk), batch 16, "
+                             "32q/8kv, D128, k16 g64"),
     ]
 }
 
@@ -196,11 +230,16 @@ def make_inputs(w: Workload, with_grad_output: bool | None = None) -> dict:
     nq = B * Hq * Sq * D
     out["Q"] = _round(normals(stream_state(w.seed, TAG_Q), nq) * w.qv_scale, w.dtype).reshape(
         B, Hq, Sq, D)
-    cen = normals(stream_state(w.seed, TAG_CENTROID), B * Hkv * (Skv // 64) * D).reshape(
-        B, Hkv, Skv // 64, 1, D)
-    noise = normals(stream_state(w.seed, TAG_K), B * Hkv * Skv * D).reshape(
-        B, Hkv, Skv // 64, 64, D)
-    K = _round((cen + 0.5 * noise).reshape(B, Hkv, Skv, D), w.dtype)
+    nch = -(-Skv // 64)   # chunks, the last one possibly partial (a decode cache)
+    cen = normals(stream_state(w.seed, TAG_CENTROID), B * Hkv * nch * D).reshape(
+        B, Hkv, nch, 1, D)
+    noise = normals(stream_state(w.seed, TAG_K), B * Hkv * Skv * D)
+    if Skv % 64 == 0:
+        K = (cen + 0.5 * noise.reshape(B, Hkv, nch, 64, D)).reshape(B, Hkv, Skv, D)
+    else:
+        K = np.repeat(cen[:, :, :, 0], 64, axis=2)[:, :, :Skv] + 0.5 * noise.reshape(
+            B, Hkv, Skv, D)
+    K = _round(K, w.dtype)
     del cen, noise
     if w.dup_fraction > 0:
         _duplicate_chunks(K, w.seed, w.dup_fraction, w.dtype)

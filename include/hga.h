@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 2
+#define HGA_ABI_VERSION 3
 #define HGA_CHUNK 64      /* tokens per chunk (the page's 64-token chunks) */
 #define HGA_GROUP 8       /* tokens per group (the page's 8-token groups)  */
 #define HGA_QBLOCK 64     /* queries per routing block                      */
@@ -102,6 +102,11 @@ const char* hga_status_str(hga_status s);
 /* Host-only check of a shape against the limits above; touches no device. */
 hga_status hga_validate_shape(const hga_shape* shape);
 
+/* Host-only check of a decode shape (see hga_decode): q_len == 1,
+ * 1 <= kv_len <= HGA_MAX_KV_LEN, C = kv_capacity (kv_len when 0) a multiple
+ * of 64 in [kv_len, HGA_MAX_KV_LEN], the other fields as for any shape. */
+hga_status hga_validate_decode_shape(const hga_shape* shape);
+
 /* Chunk and group summaries of K (page section "What HGA does differently":
  * one compact summary vector per 64-token chunk stays resident in GPU memory;
  * the 8-token group summaries serve the second routing level).
@@ -110,8 +115,10 @@ hga_status hga_validate_shape(const hga_shape* shape);
  *                                            [chunk_begin, chunk_end) only
  *   group_mean [B][Hkv][C/8][D]              fp32, written for the groups of
  *                                            those chunks only
- * 0 <= chunk_begin <= chunk_end <= kv_len/64.  The range lets a caller append
- * the summaries of new chunks to a resident history without rebuilding it. */
+ * 0 <= chunk_begin <= chunk_end <= kv_len/64 (complete chunks only).  The
+ * range lets a caller append the summaries of new chunks to a resident history
+ * without rebuilding it.  A decode shape (q_len == 1, see hga_decode) is
+ * accepted too: a decoder appends chunk c once its 64 keys are in the cache. */
 hga_status hga_build_summaries(const hga_shape* shape, const void* K, float* chunk_mean,
                                float* group_mean, int32_t chunk_begin, int32_t chunk_end,
                                void* stream);
@@ -197,6 +204,44 @@ hga_status hga_attend_bwd_dkdv_range(const hga_shape* shape, const void* Q, cons
                                      const int32_t* group_idx, int32_t chunk_begin,
                                      int32_t chunk_end, void* dK, void* dV, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/* Decode: attention of one new token per (b, query head) over a resident
+ * key/value cache (page section "What HGA does differently", read for
+ * generation, which the page says HGA also serves: the newest token is a
+ * query block of one, routed over the resident summaries, and attends exact
+ * tokens only).  Routing and attention run as two kernels on `stream`.
+ *   shape      a decode shape (hga_validate_decode_shape): q_len == 1;
+ *              kv_len = L counts the new token, whose position is p = L - 1
+ *   Q          [B][Hq][D]          dtype, the new token's queries
+ *   K, V       [B][Hkv][C][D]      dtype, rows 0..p written (row p = the new
+ *                                  token's key and value); may be pinned host
+ *                                  memory as for every call
+ *   chunk_mean [B][Hkv][C/64][D], group_mean [B][Hkv][C/8][D]  fp32: the
+ *              summaries of every chunk before the own chunk p/64 must be
+ *              built (hga_build_summaries with this shape)
+ *   chunk_idx  [B][Hq][top_k]      int32, nullable
+ *   group_idx  [B][Hq][top_g]      int32, required when top_g > 0 (written by
+ *                                  the routing, read by the attention)
+ *   O          [B][Hq][D]          dtype
+ *   lse        [B][Hq]             fp32 natural-log log-sum-exp, nullable
+ * Routing: the routing query is the token's query itself; the row keeps
+ * min(top_k, p/64) of the chunks before its own chunk, then min(top_g,
+ * 8 * kept) groups of those chunks (ascending, -1 padded, ties to the lower
+ * index).  Attention: every token of the kept groups plus the own chunk's
+ * positions 64 * (p/64) .. p.  No workspace. */
+hga_status hga_decode(const hga_shape* shape, const void* Q, const void* K, const void* V,
+                      const float* chunk_mean, const float* group_mean, int32_t* chunk_idx,
+                      int32_t* group_idx, void* O, float* lse, void* stream);
+
+/* The two halves of hga_decode, same arguments and contract, for callers that
+ * schedule them apart: the routing writes group_idx (and chunk_idx), the
+ * attention reads group_idx as written by it for the same shape.  Summaries
+ * may be NULL when kv_len <= 64 (no candidate chunk). */
+hga_status hga_decode_route(const hga_shape* shape, const void* Q, const float* chunk_mean,
+                            const float* group_mean, int32_t* chunk_idx, int32_t* group_idx,
+                            void* stream);
+hga_status hga_decode_attend(const hga_shape* shape, const void* Q, const void* K, const void* V,
+                             const int32_t* group_idx, void* O, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert hga.hga_abi_version() == 2
+    assert hga.hga_abi_version() == 3
 
 
 def _ok_shape(**kw):
@@ -116,3 +116,84 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(hga, "_lib", None)
     with pytest.raises(hga.HGAError):
         hga.hga_abi_version()
+
+
+def _dec_shape(**kw):
+    base = dict(batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128, q_len=1, kv_len=16424,
+                top_k=16, top_g=64, dtype="bf16", kv_capacity=16448)
+    base.update(kw)
+    return hga.make_shape(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    ({"kv_len": 1, "kv_capacity": 64}, 0),           # the very first token
+    ({"kv_len": 64, "kv_capacity": 0}, 0),           # capacity 0 = kv_len, a multiple of 64
+    ({"kv_len": 100, "kv_capacity": 0}, 2),          # capacity must be a multiple of 64
+    ({"kv_capacity": 16400}, 2),
+    ({"kv_capacity": 16384}, 2),                     # below kv_len
+    ({"kv_capacity": -64}, 2),
+    ({"kv_len": 0}, 2),
+    ({"q_len": 64}, 2),                              # a block shape is not a decode shape
+    ({"kv_len": 131073, "kv_capacity": 131136}, 2),
+    ({"top_g": 513}, 2),
+    ({"n_q_heads": 30}, 2),
+    ({"head_dim": 96}, 3),
+    ({"dtype": 7}, 3),
+    ({"softmax_scale": float("nan")}, 2),
+])
+def test_validate_decode_shape(kw, status):
+    assert hga.hga_validate_decode_shape(_dec_shape(**kw)) == status
+
+
+def test_block_and_decode_shapes_are_told_apart():
+    assert hga.hga_validate_shape(_dec_shape()) == 2
+    assert hga.hga_validate_decode_shape(_ok_shape()) == 2
+
+
+def test_decode_argument_errors(lib):
+    s = _dec_shape()
+    lib.hga_decode.restype = ctypes.c_int
+    lib.hga_decode.argtypes = [ctypes.POINTER(hga.HgaShape)] + [ctypes.c_void_p] * 10
+    ok = [16] * 10    # dummy non-null addresses; nothing is launched on an error
+    assert lib.hga_decode(None, *ok) == 1
+    for i in (0, 1, 2, 7):             # Q, K, V, O
+        args = list(ok)
+        args[i] = None
+        assert lib.hga_decode(ctypes.byref(s), *args) == 1
+    args = list(ok)
+    args[6] = None                      # group_idx with top_g > 0
+    assert lib.hga_decode(ctypes.byref(s), *args) == 1
+    args = list(ok)
+    args[3] = None                      # chunk summaries when there are candidates
+    assert lib.hga_decode(ctypes.byref(s), *args) == 1
+    bad = _dec_shape(kv_capacity=16400)
+    assert lib.hga_decode(ctypes.byref(bad), *ok) == 2
+    assert lib.hga_decode(ctypes.byref(_ok_shape()), *ok) == 2
+
+
+def test_build_summaries_accepts_decode_shapes_complete_chunks_only(lib):
+    s = _dec_shape()      # kv_len 16424: 256 complete chunks
+    lib.hga_build_summaries.restype = ctypes.c_int
+    assert lib.hga_build_summaries(ctypes.byref(s), 16, 16, 16, 0, 257, None) == 2
+    assert lib.hga_build_summaries(ctypes.byref(s), 16, 16, 16, 3, 3, None) == 0   # empty range
+
+
+def test_decode_halves_argument_errors(lib):
+    s = _dec_shape()
+    sp = ctypes.POINTER(hga.HgaShape)
+    lib.hga_decode_route.restype = ctypes.c_int
+    lib.hga_decode_route.argtypes = [sp] + [ctypes.c_void_p] * 6
+    lib.hga_decode_attend.restype = ctypes.c_int
+    lib.hga_decode_attend.argtypes = [sp] + [ctypes.c_void_p] * 7
+    assert lib.hga_decode_route(ctypes.byref(s), None, 16, 16, 16, 16, None) == 1     # Q
+    assert lib.hga_decode_route(ctypes.byref(s), 16, None, 16, 16, 16, None) == 1     # summaries
+    assert lib.hga_decode_route(ctypes.byref(s), 16, 16, 16, 16, None, None) == 1     # group_idx
+    assert lib.hga_decode_route(ctypes.byref(_ok_shape()), 16, 16, 16, 16, 16, None) == 2
+    # a first-chunk token has no candidates: nothing to route with budgets 0
+    first = _dec_shape(kv_len=10, kv_capacity=64, top_k=0, top_g=0)
+    assert lib.hga_decode_route(ctypes.byref(first), 16, None, None, None, None, None) == 0
+    assert lib.hga_decode_attend(ctypes.byref(s), 16, 16, 16, None, 16, 16, None) == 1  # group_idx
+    assert lib.hga_decode_attend(ctypes.byref(s), 16, None, 16, 16, 16, 16, None) == 1  # K
+    assert lib.hga_decode_attend(ctypes.byref(s), 16, 16, 16, 16, None, 16, None) == 1  # O
+    assert lib.hga_decode_attend(ctypes.byref(_ok_shape()), 16, 16, 16, 16, 16, 16, None) == 2
