@@ -1,6 +1,6 @@
 // C ABI of the HGA library: argument validation and kernel dispatch.
 // The contract of every entry point is documented in include/hga.h.
-#include "../../include/hga.h"
+#include "hga.h"
 
 #include <math.h>
 #include <string.h>

@@ -76,21 +76,6 @@ __device__ __forceinline__ float xor_sum16_32(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Sum over the wavefront, result in every lane: butterfly over lane xor 1, 2
-// (DPP quad permutes), the two quads of each 8-lane half-row (half-row
-// mirror), the two halves of each 16-lane row (row mirror), then lane xor 16
-// and xor 32 (permlane swaps).  All VALU; no LDS round trip.
-__device__ __forceinline__ int wave_sum(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-  x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
-  x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);  // row_mirror
-  const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
-  x = (int)(a[0] + a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
-  return (int)(b[0] + b[1]);
-}
-
 // Work index for block `bid` such that consecutive work indices land on the
 // same XCD.  Workgroups are dispatched round-robin over the 8 XCDs, so XCD x
 // runs bids x, x+8, ...; it receives the contiguous work range

@@ -7,8 +7,9 @@
 // within a block depends on several query positions, which is why the block
 // is routed as a whole (its routing query is the mean of its 64 queries).
 //
-// One workgroup per (b, kv head, block, set of up to 4 query heads of that kv
-// head); those rows share the candidate chunks and the summaries.
+// One workgroup per (b, kv head, block, set of RW query heads of that kv head;
+// RW = 2 by default, measured best against 1 and 4); those rows share the
+// candidate chunks and the summaries.
 //   1. each wavefront computes one row's block query (mean of its 64 query
 //      rows: 16 independent 16-byte loads per lane, then a cross-lane sum);
 //      in decode (a block of one query, QB = 1) the block query is the query;
@@ -17,13 +18,15 @@
 //      block queries stay in registers (fp32, fixed summation order); scores
 //      go to LDS;
 //   3. wavefront r selects row r's top-k by a wave-level radix select on
-//      order-preserving 32-bit keys: 32 rounds of per-lane counting and a
-//      wave-wide sum fix the k-th largest key bit by bit, ties at that key go
-//      to the lower index by a ballot prefix count, and kept indices are
-//      compacted in ascending order the same way;
-//   4. the wavefronts score the 8 groups of every kept chunk of every row
-//      (one chunk's 8 consecutive group summaries per wavefront step, scores
-//      to LDS); then wavefront r takes row r's top-g jointly with the same
+//      order-preserving 32-bit keys: the k-th largest key is fixed bit by bit
+//      from the top, each round counting the keys at or above the trial
+//      threshold with ballots and scalar popcounts, stopping as soon as exactly
+//      k keys are at or above it; ties at the threshold go to the lower index
+//      by a ballot prefix count, and kept indices are compacted in ascending
+//      order the same way;
+//   4. wavefront r scores the 8 groups of every kept chunk of row r (one
+//      chunk's 8 consecutive group summaries per step, eight steps in flight,
+//      scores to LDS), then takes row r's top-g jointly with the same
 //      selection.
 #include "hga_device.h"
 #include "hga_kernels.h"
@@ -32,7 +35,11 @@ namespace hga {
 namespace {
 
 constexpr int kMaxTopK = 64;
-constexpr int kRowsPerWG = 4;
+#ifndef HGA_ROUTE_CHUNK_UNROLL
+#define HGA_ROUTE_CHUNK_UNROLL 4
+#endif
+constexpr int kChunkUnroll = HGA_ROUTE_CHUNK_UNROLL;   // chunk-summary steps in flight per wavefront
+constexpr int kGroupUnroll = 8;                        // group-summary steps in flight per wavefront
 
 struct RouteP {
   const void* Q;
@@ -68,21 +75,35 @@ __device__ __forceinline__ void select_best(const uint32_t (&key)[NS], int n, in
     for (int j = 0; j < NS; ++j) sel[j] = false;
     return;
   }
-  // largest threshold T with #{key >= T} >= kk, i.e. the kk-th largest key
-  // (counted per lane in VALU registers, then one wave-wide sum per round: a
-  // ballot per slot would chain every compare through the VCC register)
+  // largest threshold T with #{key >= T} >= kk, i.e. the kk-th largest key,
+  // fixed bit by bit from the top.  The wave-wide counts are popcounts of
+  // ballots (scalar unit), so T stays in a scalar register; with few slots one
+  // ballot per slot, with many a per-lane count and one ballot per bit of it.
+  // Once exactly kk keys are >= T the kept set is decided: every key >= T,
+  // which the tie step below also yields (it keeps all keys equal to T).
   uint32_t T = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t trial = T | (1u << bit);
-    int c = 0;
+    int tot = 0;
+    if constexpr (NS <= 8) {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) c += key[j] >= trial ? 1 : 0;
-    if (wave_sum(c) >= kk) T = trial;
+      for (int j = 0; j < NS; ++j) tot += __popcll(__ballot(key[j] >= trial));
+    } else {
+      constexpr int NB = NS < 16 ? 4 : NS < 32 ? 5 : 6;   // bits of a count <= NS
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) c += key[j] >= trial ? 1 : 0;
+#pragma unroll
+      for (int q = 0; q < NB; ++q) tot += __popcll(__ballot((c >> q) & 1)) << q;
+    }
+    if (tot >= kk) {
+      T = trial;
+      if (tot == kk) break;
+    }
   }
-  int gl = 0;
+  int gt = 0;
 #pragma unroll
-  for (int j = 0; j < NS; ++j) gl += key[j] > T ? 1 : 0;
-  const int gt = wave_sum(gl);
+  for (int j = 0; j < NS; ++j) gt += __popcll(__ballot(key[j] > T));
   const int need = kk - gt;  // how many of the candidates equal to T are kept
   int eq_before = 0;
 #pragma unroll
@@ -119,14 +140,17 @@ __device__ __forceinline__ float sum8(float v) {
   return v;
 }
 
-template <typename T, int D, int QB, int NSC, int NSG>
+template <typename T, int D, int QB, int RW, int NSC, int NSG>
 __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
   constexpr int kGroupSlots = NSG;   // group candidates per row: up to 64 * NSG
   constexpr int kMaxChunks = 64 * NSC;
-  __shared__ __attribute__((aligned(16))) float s_qbar[kRowsPerWG][D];
-  __shared__ float s_score[kRowsPerWG][kMaxChunks];
-  __shared__ int s_chunk[kRowsPerWG][kMaxTopK];
-  __shared__ float s_gscore[kRowsPerWG][8 * kMaxTopK];
+  constexpr int kWaves = kThreads / 64;
+  constexpr int WPR = kWaves / RW;   // wavefronts scoring one row's groups
+  static_assert(RW >= 1 && RW <= kWaves && kWaves % RW == 0, "rows per workgroup");
+  __shared__ __attribute__((aligned(16))) float s_qbar[RW][D];
+  __shared__ float s_score[RW][kMaxChunks];
+  __shared__ int s_chunk[RW][kMaxTopK];
+  __shared__ float s_gscore[RW][8 * kMaxTopK];
 
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   // work: (b, hkv, block, set of query heads); sets of one kv head run on one XCD
@@ -138,8 +162,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
   const int blk = t % p.nblk;
   t /= p.nblk;
   const int hkv = t % p.Hkv, b = t / p.Hkv;
-  const int h0 = set * kRowsPerWG;                       // first query head of the set (within the group)
-  const int nrows = min(kRowsPerWG, r - h0);             // rows of this set
+  const int h0 = set * RW;                               // first query head of the set (within the group)
+  const int nrows = min(RW, r - h0);                     // rows of this set
   const int cb = p.q0 / kChunk + blk;                    // the block's own chunk = number of candidates
   const long long nch = p.Scap / kChunk;   // chunk rows per (b, kv head) in the summaries
 
@@ -193,26 +217,33 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
   //    order, then a fixed 8-lane reduction.
   constexpr int kV = D / 32;                  // float4s per lane per summary row
   const int j8 = lane & 7, rsub = lane >> 3;
-  float4 qv[kRowsPerWG][kV];
+  float4 qv[RW][kV];
 #pragma unroll
-  for (int q = 0; q < kRowsPerWG; ++q)
+  for (int q = 0; q < RW; ++q)
 #pragma unroll
     for (int m = 0; m < kV; ++m)
       qv[q][m] = reinterpret_cast<const float4*>(&s_qbar[q][0])[j8 + 8 * m];
   {
+    // kChunkUnroll steps per batch: all their loads are issued before the first use
     const float* cmb = p.cm + ((long long)b * p.Hkv + hkv) * nch * D;
-    for (int c0 = 8 * wv; c0 < cb; c0 += 32) {
-      const int c = c0 + rsub;
-      const bool live = c < cb;
-      const float4* kr = reinterpret_cast<const float4*>(cmb + (long long)(live ? c : 0) * D);
-      float4 x[kV];
+    for (int c0 = 8 * wv; c0 < cb; c0 += 32 * kChunkUnroll) {
+      float4 x[kChunkUnroll][kV];
 #pragma unroll
-      for (int m = 0; m < kV; ++m) x[m] = kr[j8 + 8 * m];
+      for (int u = 0; u < kChunkUnroll; ++u) {
+        const int c = c0 + 32 * u + rsub;
+        const float4* kr = reinterpret_cast<const float4*>(cmb + (long long)(c < cb ? c : 0) * D);
 #pragma unroll
-      for (int q = 0; q < kRowsPerWG; ++q) {
-        if (q >= nrows) break;
-        const float sc = sum8(dot4s<kV>(qv[q], x));
-        if (live && j8 == 0) s_score[q][c] = sc;
+        for (int m = 0; m < kV; ++m) x[u][m] = kr[j8 + 8 * m];
+      }
+#pragma unroll
+      for (int u = 0; u < kChunkUnroll; ++u) {
+        const int c = c0 + 32 * u + rsub;
+#pragma unroll
+        for (int q = 0; q < RW; ++q) {
+          if (q >= nrows) break;
+          const float sc = sum8(dot4s<kV>(qv[q], x[u]));
+          if (c < cb && j8 == 0) s_score[q][c] = sc;
+        }
       }
     }
   }
@@ -249,29 +280,56 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
       for (int i = kk + lane; i < p.top_k; i += 64) p.cidx[orow * p.top_k + i] = -1;
   }
   if (!p.gidx) return;
-  __syncthreads();
+  if constexpr (WPR == 1) {
+    if (wv >= nrows) return;   // row wv is scored and selected by wavefront wv alone
+    // row wv's kept chunks were written by other lanes of this wavefront
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
 
-  // 4a. group scores of every row of the set: one wavefront step covers the
-  //     8 groups of one kept chunk of one row (8 consecutive summary rows);
-  //     candidate i = 8 * (rank of the kept chunk) + group in chunk
+  // 4a. group scores: the WPR wavefronts wv = q + RW * wr of row q score its
+  //     kept chunks wr, wr + WPR, ...; one step covers the 8 groups of one
+  //     kept chunk (8 consecutive summary rows), and kGroupUnroll steps are
+  //     issued before the first use.  Candidate i = 8 * (rank of the kept
+  //     chunk) + group in chunk.
   {
-    const float* gmb = p.gm + ((long long)b * p.Hkv + hkv) * nch * 8 * D;
+    const int q = wv % RW, wr = wv / RW;
+    if (q < nrows) {
+      const float* gmb = p.gm + ((long long)b * p.Hkv + hkv) * nch * 8 * D;
+      float4 qw[kV];
 #pragma unroll
-    for (int q = 0; q < kRowsPerWG; ++q) {
-      if (q >= nrows) break;
-      for (int i = wv; i < kk; i += 4) {
-        const int g = s_chunk[q][i] * 8 + rsub;
-        const float4* gr = reinterpret_cast<const float4*>(gmb + (long long)g * D);
-        float4 x[kV];
+      for (int m = 0; m < kV; ++m) qw[m] = reinterpret_cast<const float4*>(&s_qbar[q][0])[j8 + 8 * m];
+      for (int i0 = wr; i0 < kk; i0 += WPR * kGroupUnroll) {
+        float4 x[kGroupUnroll][kV];
 #pragma unroll
-        for (int m = 0; m < kV; ++m) x[m] = gr[j8 + 8 * m];
-        const float sc = sum8(dot4s<kV>(qv[q], x));
-        if (j8 == 0) s_gscore[q][8 * i + rsub] = sc;
+        for (int u = 0; u < kGroupUnroll; ++u) {
+          const int i = i0 + WPR * u;
+          const int g = (i < kk ? s_chunk[q][i] : 0) * 8 + rsub;
+          const float4* gr = reinterpret_cast<const float4*>(gmb + (long long)g * D);
+#pragma unroll
+          for (int m = 0; m < kV; ++m) x[u][m] = gr[j8 + 8 * m];
+        }
+#pragma unroll
+        for (int u = 0; u < kGroupUnroll; ++u) {
+          const int i = i0 + WPR * u;
+          const float sc = sum8(dot4s<kV>(qw, x[u]));
+          if (i < kk && j8 == 0) s_gscore[q][8 * i + rsub] = sc;
+        }
       }
     }
   }
-  __syncthreads();
-  if (wv >= nrows) return;   // no barrier below
+  if constexpr (WPR == 1) {
+    // the scores of row wv were written by other lanes of this wavefront
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+    if (wv >= nrows) return;   // no barrier below
+  }
 
   // 4b. joint top-g of row wv over its 8 * kk group candidates
   {
@@ -298,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
   }
 }
 
-template <typename T, int D, int QB, int NSC, int NSG>
+template <typename T, int D, int QB, int RW, int NSC, int NSG>
 hipError_t run(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
                int32_t* gi, hipStream_t s) {
   RouteP p;
@@ -306,36 +364,43 @@ hipError_t run(const Dims& d, const void* Q, const float* cm, const float* gm, i
   p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.Scap = d.Scap; p.q0 = d.q0;
   p.nblk = d.nblk; p.top_k = d.top_k; p.top_g = d.top_g;
   const int r = d.Hq / d.Hkv;
-  p.nsets = (r + kRowsPerWG - 1) / kRowsPerWG;
+  p.nsets = (r + RW - 1) / RW;
   p.nwork = d.B * d.Hkv * d.nblk * p.nsets;
-  route_kernel<T, D, QB, NSC, NSG><<<p.nwork, kThreads, 0, s>>>(p);
+  route_kernel<T, D, QB, RW, NSC, NSG><<<p.nwork, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
-template <typename T, int D, int QB, int NSC>
+template <typename T, int D, int QB, int RW, int NSC>
 hipError_t run_g(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
                  int32_t* gi, hipStream_t s) {
   // 8 * top_k group candidates per row at most
-  if (d.top_k <= 8) return run<T, D, QB, NSC, 1>(d, Q, cm, gm, ci, gi, s);
-  if (d.top_k <= 16) return run<T, D, QB, NSC, 2>(d, Q, cm, gm, ci, gi, s);
-  if (d.top_k <= 32) return run<T, D, QB, NSC, 4>(d, Q, cm, gm, ci, gi, s);
-  return run<T, D, QB, NSC, 8>(d, Q, cm, gm, ci, gi, s);
+  if (d.top_k <= 8) return run<T, D, QB, RW, NSC, 1>(d, Q, cm, gm, ci, gi, s);
+  if (d.top_k <= 16) return run<T, D, QB, RW, NSC, 2>(d, Q, cm, gm, ci, gi, s);
+  if (d.top_k <= 32) return run<T, D, QB, RW, NSC, 4>(d, Q, cm, gm, ci, gi, s);
+  return run<T, D, QB, RW, NSC, 8>(d, Q, cm, gm, ci, gi, s);
 }
 
-template <typename T, int D, int QB>
+template <typename T, int D, int QB, int RW>
 hipError_t run_c(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
                  int32_t* gi, hipStream_t s) {
   const int max_cand = (d.Skv - 1) / kChunk;   // chunks before the last query's own chunk
-  if (max_cand <= 256) return run_g<T, D, QB, 4>(d, Q, cm, gm, ci, gi, s);
-  if (max_cand <= 1024) return run_g<T, D, QB, 16>(d, Q, cm, gm, ci, gi, s);
-  return run_g<T, D, QB, 32>(d, Q, cm, gm, ci, gi, s);
+  if (max_cand <= 256) return run_g<T, D, QB, RW, 4>(d, Q, cm, gm, ci, gi, s);
+  if (max_cand <= 1024) return run_g<T, D, QB, RW, 16>(d, Q, cm, gm, ci, gi, s);
+  return run_g<T, D, QB, RW, 32>(d, Q, cm, gm, ci, gi, s);
 }
+
+#ifndef HGA_ROUTE_ROWS_BLOCK
+#define HGA_ROUTE_ROWS_BLOCK 2
+#endif
+#ifndef HGA_ROUTE_ROWS_DECODE
+#define HGA_ROUTE_ROWS_DECODE 2
+#endif
 
 template <typename T, int D>
 hipError_t run_d(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
                  int32_t* gi, hipStream_t s) {
-  return d.Sq == 1 ? run_c<T, D, 1>(d, Q, cm, gm, ci, gi, s)
-                   : run_c<T, D, kChunk>(d, Q, cm, gm, ci, gi, s);
+  return d.Sq == 1 ? run_c<T, D, 1, HGA_ROUTE_ROWS_DECODE>(d, Q, cm, gm, ci, gi, s)
+                   : run_c<T, D, kChunk, HGA_ROUTE_ROWS_BLOCK>(d, Q, cm, gm, ci, gi, s);
 }
 
 }  // namespace
