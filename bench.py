@@ -7,9 +7,16 @@ the backward (dQ, then dK/dV).  Workload: a 2048-query segment at the end of a
 top-k 16 chunks, top-g 64 groups, bf16, seeded synthetic inputs.  Inputs are
 resident in HBM before the timed region.
 
-Prints one JSON line: throughput in query tokens/s, per-phase kernel times from
-HIP events on the stream the kernels run on, the roofline of the dominant
-kernel, and the CPU oracle timed on a bounded sample of the same workload.
+The timed region replays the step from a HIP graph (the kernels allocate and
+clear nothing, so a replay is the eager step without host launch gaps); the
+eager step time is reported beside it.  Per-phase times come from HIP events
+around each kernel in an eager pass (each includes its launch gap).  The
+roofline kernel's duration comes from 20 back-to-back launches of that kernel
+alone in one graph, with HIP events on the replay stream.
+
+Prints one JSON line: throughput in query tokens/s, per-phase kernel times, the
+roofline of the dominant kernel, and the CPU oracle timed on a bounded sample
+of the same workload.  --decode and --segments select the other two workloads.
 """
 from __future__ import annotations
 
@@ -226,6 +233,70 @@ def segments_main(args):
     print(json.dumps(out))
 
 
+def graph_of(fn, copies: int = 1):
+    """`fn` (which launches on the current stream) captured `copies` times into
+    one HIP graph (torch.cuda.CUDAGraph).  The kernels allocate nothing and
+    clear nothing with memset, so a replay repeats the eager work exactly."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(copies):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def timed_replays(g, steps: int, warmup: int) -> float:
+    """Milliseconds per replay of `g` over `steps` replays (after `warmup`),
+    bracketed by device synchronisations."""
+    import torch
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def kernel_us(fn, launches: int = 20, reps: int = 5) -> float:
+    """Average duration of one launch of `fn`: `launches` back-to-back copies in
+    one graph (no host launch gaps), HIP events around each replay on the
+    replay stream, averaged over `reps` replays."""
+    import torch
+    g = graph_of(fn, launches)
+    g.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    tot = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        tot += e0.elapsed_time(e1)
+    return tot * 1e3 / (reps * launches)
+
+
+def calibration_copy(dev):
+    """One plain 256 MiB device-to-device copy (a known read and write volume
+    for scaling the memory counters)."""
+    import torch
+    src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def decode_work(w, kept_groups: int) -> dict:
     """Per-launch algorithmic bytes of the two decode kernels.  Routing: the
     queries, the chunk summaries before the own chunk (read once for the query
@@ -313,41 +384,47 @@ def decode_main(args):
     gi = torch.empty(B, Hq, w.top_g, dtype=torch.int32, device=dev)
     O = torch.empty(B, Hq, D, dtype=edt, device=dev)
     lse = torch.empty(B, Hq, device=dev)
-    stream = torch.cuda.current_stream()
+    # host-resident K/V: pass their GPU addresses (resolved once, outside any capture)
+    Ka, Va = (hga._ptr(K, "K", host_ok=True), hga._ptr(V, "V", host_ok=True)) if args.host_kv \
+        else (K, V)
+    phases = ["decode_route", "decode_attend"]
+    calls = {"decode_route": lambda: hga.hga_decode_route(s, Q, cm, gm, ci, gi),
+             "decode_attend": lambda: hga.hga_decode_attend(s, Q, Ka, Va, gi, O, lse)}
 
     def step(ev=None):
-        if ev: ev[0].record(stream)
-        hga.hga_decode_route(s, Q, cm, gm, ci, gi, stream=stream)
-        if ev: ev[1].record(stream)
-        hga.hga_decode_attend(s, Q, K, V, gi, O, lse, stream=stream)
-        if ev: ev[2].record(stream)
+        stream = torch.cuda.current_stream()
+        for i, p in enumerate(phases):
+            if ev: ev[i].record(stream)
+            calls[p]()
+        if ev: ev[len(phases)].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.calibrate_copy:
+        calibration_copy(dev)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(evs[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    phases = ["decode_route", "decode_attend"]
-    phase_ms = {p: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
-                for i, p in enumerate(phases)}
+    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the timed region: the step replayed from a HIP graph (a serving loop's form)
+    ms_step = timed_replays(graph_of(step), args.steps, args.warmup)
     kept = int((gi >= 0).sum().item())
     work = decode_work(w, kept)
     rep = {}
     for p in phases:
-        ach = work[p] / (phase_ms[p] * 1e-3) / 1e9
-        rep[p] = {"us": round(phase_ms[p] * 1e3, 2), "bound": "hbm",
+        us = kernel_us(calls[p])
+        ach = work[p] / (us * 1e-6) / 1e9
+        rep[p] = {"us": round(us, 2), "bound": "hbm",
                   "algorithmic_bytes": work[p], "achieved_GBs": round(ach, 1),
                   "frac": round(ach / PEAK_HBM_GBS, 4)}
     dom = "decode_attend"
-    ach = work[dom] / (phase_ms[dom] * 1e-3) / 1e9
+    ach = work[dom] / (rep[dom]["us"] * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": ach / PEAK_HBM_GBS, "traffic": None if args.host_kv else load_traffic(dom),
-            "kernel": dom, "algorithmic_per_launch": work[dom]}
+            "kernel": dom, "kernel_us": rep[dom]["us"], "algorithmic_per_launch": work[dom]}
     base = None
     if not args.no_cpu_baseline:
         base = cpu_baseline_decode(w, x, cm.cpu().numpy().astype(np.float64),
@@ -361,6 +438,7 @@ def decode_main(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "eager_ms_per_step": eager_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -416,46 +494,44 @@ def main():
     dK = torch.empty(sz["kv"], dtype=edt, device=dev)
     dV = torch.empty(sz["kv"], dtype=edt, device=dev)
     ws = torch.empty(hga.hga_attend_bwd_workspace(s), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
     phases = ["summaries", "route", "attend_fwd", "attend_bwd_dq", "attend_bwd_dkdv"]
+    calls = {
+        "summaries": lambda: hga.hga_build_summaries(s, t["K"], cm, gm),
+        "route": lambda: hga.hga_route(s, t["Q"], cm, gm, ci, gi),
+        "attend_fwd": lambda: hga.hga_attend_fwd(s, t["Q"], t["K"], t["V"], gi, O, lse),
+        "attend_bwd_dq": lambda: hga.hga_attend_bwd_dq(s, t["Q"], t["K"], t["V"], O, lse,
+                                                       t["dO"], gi, dQ, ws),
+        "attend_bwd_dkdv": lambda: hga.hga_attend_bwd_dkdv(s, t["Q"], t["K"], t["V"], lse,
+                                                           t["dO"], gi, dK, dV, ws),
+    }
 
     def step(ev=None):
-        if ev: ev[0].record(stream)
-        hga.hga_build_summaries(s, t["K"], cm, gm, stream=stream)
-        if ev: ev[1].record(stream)
-        hga.hga_route(s, t["Q"], cm, gm, ci, gi, stream=stream)
-        if ev: ev[2].record(stream)
-        hga.hga_attend_fwd(s, t["Q"], t["K"], t["V"], gi, O, lse, stream=stream)
-        if ev: ev[3].record(stream)
-        hga.hga_attend_bwd_dq(s, t["Q"], t["K"], t["V"], O, lse, t["dO"], gi, dQ, ws,
-                              stream=stream)
-        if ev: ev[4].record(stream)
-        hga.hga_attend_bwd_dkdv(s, t["Q"], t["K"], t["V"], lse, t["dO"], gi, dK, dV, ws,
-                                stream=stream)
-        if ev: ev[5].record(stream)
+        # every call launches on the current stream (the capture stream inside
+        # a graph capture)
+        stream = torch.cuda.current_stream()
+        for i, p in enumerate(phases):
+            if ev: ev[i].record(stream)
+            calls[p]()
+        if ev: ev[len(phases)].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     if args.calibrate_copy:
-        src = torch.ones(64 * 1024 * 1024, dtype=f32, device=dev)   # 256 MiB
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(dev)
 
+    # eager pass: per-phase HIP events (each phase includes its launch gap)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(evs[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    ms_step = wall * 1e3 / args.steps
+    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     phase_ms = {p: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
                 for i, p in enumerate(phases)}
+    # the timed region: the step replayed from a HIP graph
+    ms_step = timed_replays(graph_of(step), args.steps, args.warmup)
     pairs = attended_pairs(gi)
     work = algorithmic_work(w, pairs)
     phase_rep = {}
@@ -473,7 +549,8 @@ def main():
                             "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
     dom = max(phases, key=lambda p: phase_ms[p])
     kind, amount = work[dom]
-    sec = phase_ms[dom] * 1e-3
+    dom_us = kernel_us(calls[dom])
+    sec = dom_us * 1e-6
     if kind == "hbm":
         roof = {"bound": "hbm", "achieved": amount / sec / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
@@ -483,6 +560,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = load_traffic(dom)
     roof["kernel"] = dom
+    roof["kernel_us"] = round(dom_us, 2)
     roof["algorithmic_per_launch"] = amount
 
     base = None
@@ -497,6 +575,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "eager_ms_per_step": eager_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
