@@ -46,6 +46,7 @@ def _load():
         i = ctypes.c_int
         lib.hgao_summaries.argtypes = [i, i, i, i, i, i, _dp, _dp, _dp]
         lib.hgao_route.argtypes = [i] * 10 + [_dp, _dp, _dp, _ip, _ip, _ip, _dp, _dp]
+        lib.hgao_route_causal.argtypes = [i] * 10 + [_dp, _dp, _dp, _dp, _ip, _ip, _ip, _dp, _dp]
         lib.hgao_attend_fwd.argtypes = [i] * 9 + [ctypes.c_double, _dp, _dp, _dp, _ip, _dp, _dp]
         lib.hgao_attend_bwd.argtypes = ([i] * 9 + [ctypes.c_double, _dp, _dp, _dp, _ip, _dp,
                                                    _dp, _dp, _dp])
@@ -85,12 +86,15 @@ def summaries(K, C: int = 64, G: int = 8):
 
 
 def route(Q, chunk_mean, group_mean, Skv: int, top_k: int, top_g: int, C: int = 64,
-          G: int = 8, forced_chunk_idx=None, want_scores: bool = False):
+          G: int = 8, forced_chunk_idx=None, want_scores: bool = False, causal: bool = False,
+          Qprev=None):
     """Routing indices for every (b, hq, block).
 
     Returns ``(chunk_idx, group_idx)`` or, with ``want_scores``,
     ``(chunk_idx, group_idx, chunk_score, group_score)`` where the scores are
-    fp64 with NaN at non-candidates.
+    fp64 with NaN at non-candidates.  With ``causal`` a block is routed with
+    the mean of the C queries before it; ``Qprev`` [B,Hq,C,D] holds the C
+    queries before the segment (needed when Skv > Sq).
     """
     Q = _f64(Q)
     chunk_mean = _f64(chunk_mean)
@@ -106,8 +110,17 @@ def route(Q, chunk_mean, group_mean, Skv: int, top_k: int, top_g: int, C: int = 
     if forced_chunk_idx is not None:
         forced = np.ascontiguousarray(forced_chunk_idx, dtype=np.int32)
         assert forced.shape == ci.shape
-    rc = _load().hgao_route(B, Hq, Hkv, Sq, Skv, D, C, G, top_k, top_g, _d(Q), _d(chunk_mean),
-                            _d(group_mean), _i(forced), _i(ci), _i(gi), _d(cs), _d(gs))
+    if causal:
+        qp = None if Qprev is None else _f64(Qprev)
+        if qp is not None:
+            assert qp.shape == (B, Hq, C, D)
+        rc = _load().hgao_route_causal(B, Hq, Hkv, Sq, Skv, D, C, G, top_k, top_g, _d(Q), _d(qp),
+                                       _d(chunk_mean), _d(group_mean), _i(forced), _i(ci),
+                                       _i(gi), _d(cs), _d(gs))
+    else:
+        rc = _load().hgao_route(B, Hq, Hkv, Sq, Skv, D, C, G, top_k, top_g, _d(Q),
+                                _d(chunk_mean), _d(group_mean), _i(forced), _i(ci), _i(gi),
+                                _d(cs), _d(gs))
     _check(rc, "route")
     if want_scores:
         return ci, gi, cs, gs

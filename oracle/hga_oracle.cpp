@@ -25,7 +25,8 @@
  *
  * Readings taken where the page is silent (each is listed in the design notes):
  *  - summary of a chunk (and of a group) = mean of its keys;
- *  - the query side of the routing score = mean of the block's C queries;
+ *  - the query side of the routing score = mean of the block's C queries
+ *    (strictly causal variant: mean of the C queries before the block);
  *  - score = plain dot product; routing is per query head; a GQA query head hq
  *    reads kv head hq / (Hq/Hkv);
  *  - candidates are the chunks strictly before the query block's own chunk;
@@ -164,15 +165,25 @@ int hgao_summaries(int B, int Hkv, int S, int D, int C, int G, const double* K,
  * instead (used to re-derive the group choice for a given chunk set).
  * chunk_score / group_score (nullable, [B][Hq][Sq/C][Skv/C] and
  * [B][Hq][Sq/C][Skv/G]): the fp64 scores of every candidate, NaN elsewhere. */
-int hgao_route(int B, int Hq, int Hkv, int Sq, int Skv, int D, int C, int G,
-               int top_k, int top_g, const double* Q, const double* chunk_mean,
-               const double* group_mean, const int32_t* forced_chunk_idx,
-               int32_t* chunk_idx, int32_t* group_idx, double* chunk_score,
-               double* group_score) {
+/* Routing of every query block.  The block query is the mean of the block's C
+ * query vectors; with `causal` it is the mean of the C query vectors just
+ * before the block instead (the previous block of Q, or for the first block of
+ * a segment the C rows of Qprev [B][Hq][C][D]), so that no position's routing
+ * depends on a later position (page section "The one real caveat: causal
+ * leakage": a block's routing mixes several of its query positions). */
+static int route_impl(int B, int Hq, int Hkv, int Sq, int Skv, int D, int C, int G,
+                      int top_k, int top_g, const double* Q, bool causal, const double* Qprev,
+                      const double* chunk_mean, const double* group_mean,
+                      const int32_t* forced_chunk_idx, int32_t* chunk_idx, int32_t* group_idx,
+                      double* chunk_score, double* group_score) {
   if (!shape_ok(B, Hq, Hkv, Sq, Skv, D, C, G) || top_k < 0 || top_g < 0) return 2;
   if (!all_finite(Q, (long long)B * Hq * Sq * D)) return 4;
   const int r = Hq / Hkv, nblk = Sq / C, nc = Skv / C, ng = Skv / G, gpc = C / G;
   const int q0 = Skv - Sq;
+  if (causal && q0 > 0 && (top_k > 0 || top_g > 0)) {
+    if (!Qprev) return 2;
+    if (!all_finite(Qprev, (long long)B * Hq * C * D)) return 4;
+  }
   const double nan = std::nan("");
   for (int b = 0; b < B; ++b)
     for (int hq = 0; hq < Hq; ++hq) {
@@ -181,12 +192,22 @@ int hgao_route(int B, int Hq, int Hkv, int Sq, int Skv, int D, int C, int G,
         const long long row = ((long long)b * Hq + hq) * nblk + blk;
         const int cb = q0 / C + blk; /* the block's own chunk */
 
-        /* block query: mean of the block's C query vectors */
+        /* block query: mean of C query vectors (the block's own, or with
+         * `causal` the C vectors before the block); unused without candidates */
         std::vector<double> qbar(D, 0.0);
-        for (int d = 0; d < D; ++d) {
-          double s = 0.0;
-          for (int i = blk * C; i < blk * C + C; ++i) s += Q[idx4(b, hq, i, d, Hq, Sq, D)];
-          qbar[d] = s / C;
+        if (cb > 0) {
+          for (int d = 0; d < D; ++d) {
+            double s = 0.0;
+            for (int i = 0; i < C; ++i) {
+              if (!causal)
+                s += Q[idx4(b, hq, blk * C + i, d, Hq, Sq, D)];
+              else if (blk > 0)
+                s += Q[idx4(b, hq, (blk - 1) * C + i, d, Hq, Sq, D)];
+              else
+                s += Qprev[idx4(b, hq, i, d, Hq, C, D)];
+            }
+            qbar[d] = s / C;
+          }
         }
 
         /* chunk stage: candidates are the chunks strictly before cb */
@@ -234,6 +255,30 @@ int hgao_route(int B, int Hq, int Hkv, int Sq, int Skv, int D, int C, int G,
       }
     }
   return 0;
+}
+
+int hgao_route(int B, int Hq, int Hkv, int Sq, int Skv, int D, int C, int G,
+               int top_k, int top_g, const double* Q, const double* chunk_mean,
+               const double* group_mean, const int32_t* forced_chunk_idx,
+               int32_t* chunk_idx, int32_t* group_idx, double* chunk_score,
+               double* group_score) {
+  return route_impl(B, Hq, Hkv, Sq, Skv, D, C, G, top_k, top_g, Q, false, nullptr, chunk_mean,
+                    group_mean, forced_chunk_idx, chunk_idx, group_idx, chunk_score,
+                    group_score);
+}
+
+/* Strictly causal routing: as hgao_route, but block blk is routed with the
+ * mean of the C queries before it (rows (blk-1)C .. blk C - 1 of Q; for
+ * blk = 0 the C rows of Qprev, the queries just before the segment, needed
+ * only when the segment has history). */
+int hgao_route_causal(int B, int Hq, int Hkv, int Sq, int Skv, int D, int C, int G,
+                      int top_k, int top_g, const double* Q, const double* Qprev,
+                      const double* chunk_mean, const double* group_mean,
+                      const int32_t* forced_chunk_idx, int32_t* chunk_idx, int32_t* group_idx,
+                      double* chunk_score, double* group_score) {
+  return route_impl(B, Hq, Hkv, Sq, Skv, D, C, G, top_k, top_g, Q, true, Qprev, chunk_mean,
+                    group_mean, forced_chunk_idx, chunk_idx, group_idx, chunk_score,
+                    group_score);
 }
 
 /* Exact-token attention (page section "What HGA does differently": only the
