@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--host-kv", action="store_true",
                     help="with --segments or --decode: keep the keys and values in pinned "
                          "host memory")
+    ap.add_argument("--causal", action="store_true",
+                    help="strictly causal routing (block j routed with the 64 queries before it)")
     ap.add_argument("--decode", action="store_true",
                     help="decode mode: one new token per sequence over a 16,424-token cache, "
                          "batch 16 (routing + attention per step)")
@@ -116,7 +118,7 @@ def load_traffic(phase: str):
     return r.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x, budget_s: float = 12.0):
+def cpu_baseline(w, x, budget_s: float = 12.0, causal: bool = False):
     """The CPU oracle, single thread, on whole kv heads of the same inputs (each
     with its query heads: summaries, routing, attention forward and backward in
     fp64), taken one after another until `budget_s` seconds of work are done;
@@ -130,10 +132,13 @@ def cpu_baseline(w, x, budget_s: float = 12.0):
     for b, h in units:
         xs = {"Q": x["Q"][b:b + 1, h * r:(h + 1) * r], "K": x["K"][b:b + 1, h:h + 1],
               "V": x["V"][b:b + 1, h:h + 1], "dO": x["dO"][b:b + 1, h * r:(h + 1) * r]}
+        if causal:
+            xs["Qprev"] = x["Qprev"][b:b + 1, h * r:(h + 1) * r]
         xf = {k: syn.to_f64(v, w.dtype) for k, v in xs.items()}
         t0 = time.perf_counter()
         cm, gm = oracle.summaries(xf["K"])
-        _, gi = oracle.route(xf["Q"], cm, gm, w.kv_len, w.top_k, w.top_g)
+        _, gi = oracle.route(xf["Q"], cm, gm, w.kv_len, w.top_k, w.top_g, causal=causal,
+                             Qprev=xf.get("Qprev"))
         oracle.attend_fwd(xf["Q"], xf["K"], xf["V"], gi)
         oracle.attend_bwd(xf["Q"], xf["K"], xf["V"], gi, xf["dO"])
         dt += time.perf_counter() - t0
@@ -475,7 +480,7 @@ def main():
     from hierarchical_routed_sparse_amd import synthetic as syn
 
     w = syn.WORKLOADS[args.workload]
-    x = syn.make_inputs(w, with_grad_output=True)
+    x = syn.make_inputs(w, with_grad_output=True, with_qprev=args.causal)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     t = {k: syn.to_torch(v, w.dtype, dev) for k, v in x.items()}
@@ -497,7 +502,8 @@ def main():
     phases = ["summaries", "route", "attend_fwd", "attend_bwd_dq", "attend_bwd_dkdv"]
     calls = {
         "summaries": lambda: hga.hga_build_summaries(s, t["K"], cm, gm),
-        "route": lambda: hga.hga_route(s, t["Q"], cm, gm, ci, gi),
+        "route": (lambda: hga.hga_route_causal(s, t["Q"], t["Qprev"], cm, gm, ci, gi))
+        if args.causal else (lambda: hga.hga_route(s, t["Q"], cm, gm, ci, gi)),
         "attend_fwd": lambda: hga.hga_attend_fwd(s, t["Q"], t["K"], t["V"], gi, O, lse),
         "attend_bwd_dq": lambda: hga.hga_attend_bwd_dq(s, t["Q"], t["K"], t["V"], O, lse,
                                                        t["dO"], gi, dQ, ws),
@@ -565,10 +571,10 @@ def main():
 
     base = None
     if not args.no_cpu_baseline:
-        base = cpu_baseline(w, x)
+        base = cpu_baseline(w, x, causal=args.causal)
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC + (" (strictly causal routing)" if args.causal else ""),
         "value": w.batch * w.q_len / (ms_step * 1e-3),
         "unit": "query tokens/s",
         "n_gpus": 1,
@@ -582,7 +588,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded clustered keys, N(0,1)/sqrt(128) queries and values)",
         "config": {
-            "workload": f"{w.name} fwd+bwd",
+            "workload": f"{w.name} fwd+bwd" + (", strictly causal routing" if args.causal else ""),
             "batch": w.batch, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "q_len": w.q_len, "kv_len": w.kv_len,
             "chunk": 64, "group": 8, "top_k": w.top_k, "top_g": w.top_g,

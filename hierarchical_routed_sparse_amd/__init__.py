@@ -24,7 +24,7 @@ import os
 
 __all__ = [
     "HGAError", "HgaShape", "make_shape", "lib_path", "hga_abi_version", "hga_validate_shape",
-    "hga_build_summaries", "hga_route", "hga_attend_fwd", "hga_attend_bwd_workspace",
+    "hga_build_summaries", "hga_route", "hga_route_causal", "hga_attend_fwd", "hga_attend_bwd_workspace",
     "hga_attend_bwd", "hga_attend_bwd_dq", "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range",
     "hga_validate_decode_shape", "hga_decode", "hga_decode_route", "hga_decode_attend",
     "forward", "backward", "decode",
@@ -87,6 +87,7 @@ def _load():
     lib.hga_validate_shape.argtypes = [_SP]
     lib.hga_build_summaries.argtypes = [_SP, _vp, _vp, _vp, i32, i32, _vp]
     lib.hga_route.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.hga_route_causal.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.hga_attend_fwd.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.hga_attend_bwd_workspace.argtypes = [_SP, ctypes.POINTER(sz)]
     lib.hga_attend_bwd.argtypes = [_SP] + [_vp] * 11 + [sz, _vp]
@@ -97,7 +98,7 @@ def _load():
     lib.hga_decode.argtypes = [_SP] + [_vp] * 10
     lib.hga_decode_route.argtypes = [_SP] + [_vp] * 6
     lib.hga_decode_attend.argtypes = [_SP] + [_vp] * 7
-    for name in ("hga_validate_shape", "hga_validate_decode_shape", "hga_decode",
+    for name in ("hga_validate_shape", "hga_validate_decode_shape", "hga_decode", "hga_route_causal",
                  "hga_decode_route", "hga_decode_attend", "hga_build_summaries", "hga_route", "hga_attend_fwd",
                  "hga_attend_bwd_workspace", "hga_attend_bwd", "hga_attend_bwd_dq",
                  "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range"):
@@ -199,6 +200,7 @@ def _sizes(s: HgaShape):
         ci=(s.batch, s.n_q_heads, nblk, s.top_k),
         gi=(s.batch, s.n_q_heads, nblk, s.top_g),
         lse=(s.batch, s.n_q_heads, s.q_len),
+        qprev=(s.batch, s.n_q_heads, QBLOCK, s.head_dim),
     )
 
 
@@ -241,6 +243,23 @@ def hga_route(shape, Q, chunk_mean, group_mean, chunk_idx, group_idx, stream=Non
         _ptr(chunk_idx, "chunk_idx", torch.int32, sz["ci"], nullable=True),
         _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
         _stream(stream)), "hga_route")
+
+
+def hga_route_causal(shape, Q, Q_prev, chunk_mean, group_mean, chunk_idx, group_idx,
+                     stream=None):
+    """Strictly causal routing: block j routed with the mean of the 64 queries
+    before it; Q_prev [B,Hq,64,D] holds the 64 queries before the segment
+    (None when kv_len == q_len)."""
+    import torch
+    sz, dt = _sizes(shape), _elt_dtype(shape)
+    _check(_load().hga_route_causal(
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]),
+        _ptr(Q_prev, "Q_prev", dt, sz["qprev"], nullable=True),
+        _ptr(chunk_mean, "chunk_mean", torch.float32, sz["cm"]),
+        _ptr(group_mean, "group_mean", torch.float32, sz["gm"], nullable=True),
+        _ptr(chunk_idx, "chunk_idx", torch.int32, sz["ci"], nullable=True),
+        _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        _stream(stream)), "hga_route_causal")
 
 
 def hga_attend_fwd(shape, Q, K, V, group_idx, O, lse=None, stream=None):
@@ -366,9 +385,10 @@ def hga_decode_attend(shape, Q, K, V, group_idx, O, lse=None, stream=None):
 
 # ------------------------------------------------------------------ compositions
 
-def forward(shape, Q, K, V, stream=None):
-    """Summaries, routing and attention with freshly allocated outputs.
-    Returns dict(chunk_mean, group_mean, chunk_idx, group_idx, O, lse)."""
+def forward(shape, Q, K, V, stream=None, causal=False, Q_prev=None):
+    """Summaries, routing and attention with freshly allocated outputs (with
+    ``causal``: strictly causal routing, ``Q_prev`` the 64 queries before the
+    segment).  Returns dict(chunk_mean, group_mean, chunk_idx, group_idx, O, lse)."""
     import torch
     sz = _sizes(shape)
     dev = Q.device
@@ -381,8 +401,12 @@ def forward(shape, Q, K, V, stream=None):
         lse=torch.empty(sz["lse"], dtype=torch.float32, device=dev),
     )
     hga_build_summaries(shape, K, out["chunk_mean"], out["group_mean"], stream=stream)
-    hga_route(shape, Q, out["chunk_mean"], out["group_mean"], out["chunk_idx"],
-              out["group_idx"], stream=stream)
+    if causal:
+        hga_route_causal(shape, Q, Q_prev, out["chunk_mean"], out["group_mean"],
+                         out["chunk_idx"], out["group_idx"], stream=stream)
+    else:
+        hga_route(shape, Q, out["chunk_mean"], out["group_mean"], out["chunk_idx"],
+                  out["group_idx"], stream=stream)
     hga_attend_fwd(shape, Q, K, V, out["group_idx"], out["O"], out["lse"], stream=stream)
     return out
 

@@ -137,7 +137,23 @@ hga_status hga_route(const hga_shape* shape, const void* Q, const float* chunk_m
   if (!Q || !chunk_mean) return HGA_ERR_NULL;
   if (shape->top_g > 0 && (!group_idx || !group_mean)) return HGA_ERR_NULL;
   if (shape->top_k == 0 && shape->top_g == 0 && !group_idx && !chunk_idx) return HGA_OK;
-  return from_hip(hga::launch_route(dims_of(shape), Q, chunk_mean, group_mean,
+  return from_hip(hga::launch_route(dims_of(shape), Q, nullptr, false, chunk_mean, group_mean,
+                                    shape->top_k > 0 ? chunk_idx : nullptr,
+                                    shape->top_g > 0 ? group_idx : nullptr,
+                                    (hipStream_t)stream));
+}
+
+hga_status hga_route_causal(const hga_shape* shape, const void* Q, const void* Q_prev,
+                            const float* chunk_mean, const float* group_mean,
+                            int32_t* chunk_idx, int32_t* group_idx, void* stream) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!Q || !chunk_mean) return HGA_ERR_NULL;
+  if (shape->top_g > 0 && (!group_idx || !group_mean)) return HGA_ERR_NULL;
+  const bool routes = shape->top_k > 0 || shape->top_g > 0;
+  if (routes && shape->kv_len > shape->q_len && !Q_prev) return HGA_ERR_NULL;
+  if (!routes && !group_idx && !chunk_idx) return HGA_OK;
+  return from_hip(hga::launch_route(dims_of(shape), Q, Q_prev, true, chunk_mean, group_mean,
                                     shape->top_k > 0 ? chunk_idx : nullptr,
                                     shape->top_g > 0 ? group_idx : nullptr,
                                     (hipStream_t)stream));
@@ -231,7 +247,7 @@ hga_status hga_decode_route(const hga_shape* shape, const void* Q, const float* 
   if (candidates && (!chunk_mean || (shape->top_g > 0 && !group_mean))) return HGA_ERR_NULL;
   if (shape->top_k == 0 && shape->top_g == 0) return HGA_OK;
   // launched also without candidates: it then writes the -1 padding
-  return from_hip(hga::launch_route(dims_of(shape), Q, chunk_mean, group_mean,
+  return from_hip(hga::launch_route(dims_of(shape), Q, nullptr, false, chunk_mean, group_mean,
                                     shape->top_k > 0 ? chunk_idx : nullptr,
                                     shape->top_g > 0 ? group_idx : nullptr,
                                     (hipStream_t)stream));

@@ -19,9 +19,11 @@ struct Dims {
 hipError_t launch_summaries(const Dims& d, const void* K, float* chunk_mean, float* group_mean,
                             int chunk_begin, int chunk_end, hipStream_t s);
 
-hipError_t launch_route(const Dims& d, const void* Q, const float* chunk_mean,
-                        const float* group_mean, int32_t* chunk_idx, int32_t* group_idx,
-                        hipStream_t s);
+// causal: route block j with the mean of the 64 queries before it (Q_prev
+// [B][Hq][64][D] = the 64 queries before the segment, for its first block).
+hipError_t launch_route(const Dims& d, const void* Q, const void* Q_prev, bool causal,
+                        const float* chunk_mean, const float* group_mean, int32_t* chunk_idx,
+                        int32_t* group_idx, hipStream_t s);
 
 hipError_t launch_attend_fwd(const Dims& d, const void* Q, const void* K, const void* V,
                              const int32_t* group_idx, void* O, float* lse, hipStream_t s);

@@ -43,6 +43,8 @@ constexpr int kGroupUnroll = 8;                        // group-summary steps in
 
 struct RouteP {
   const void* Q;
+  const void* Qprev;   // causal: the 64 queries before the segment, [B][Hq][64][D]
+  int causal;          // route block j with the mean of the 64 queries before it
   const float* cm;
   const float* gm;
   int32_t* cidx;
@@ -178,9 +180,17 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) s_qbar[wv][8 * lane + e] = to_f32(v[e]);
     }
+  } else if (wv < nrows && p.causal && cb == 0) {
+    // strictly causal, first block of a sequence: no candidates, no routing query
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) s_qbar[wv][lane + 64 * e] = 0.f;
   } else if (wv < nrows) {
     const int hq = hkv * r + h0 + wv;
-    const T* Qb = reinterpret_cast<const T*>(p.Q) + (((long long)b * p.Hq + hq) * p.Sq + (long long)blk * kChunk) * D;
+    // the block's own 64 queries; strictly causal: the 64 queries before the
+    // block (the previous block, or before the segment's first block)
+    const T* Qb = !p.causal ? reinterpret_cast<const T*>(p.Q) + (((long long)b * p.Hq + hq) * p.Sq + (long long)blk * kChunk) * D
+                : blk > 0   ? reinterpret_cast<const T*>(p.Q) + (((long long)b * p.Hq + hq) * p.Sq + (long long)(blk - 1) * kChunk) * D
+                            : reinterpret_cast<const T*>(p.Qprev) + ((long long)b * p.Hq + hq) * kChunk * D;
     constexpr int kOct = D / 8;                 // 8-element columns
     constexpr int kRowSets = 64 / kOct;         // lanes along the rows
     constexpr int kRowsPerLane = kChunk / kRowSets;
@@ -357,10 +367,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
 }
 
 template <typename T, int D, int QB, int RW, int NSC, int NSG>
-hipError_t run(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
-               int32_t* gi, hipStream_t s) {
+hipError_t run(const Dims& d, const void* Q, const void* Qprev, int causal, const float* cm,
+               const float* gm, int32_t* ci, int32_t* gi, hipStream_t s) {
   RouteP p;
-  p.Q = Q; p.cm = cm; p.gm = gm; p.cidx = ci; p.gidx = gi;
+  p.Q = Q; p.Qprev = Qprev; p.causal = causal; p.cm = cm; p.gm = gm; p.cidx = ci; p.gidx = gi;
   p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.Scap = d.Scap; p.q0 = d.q0;
   p.nblk = d.nblk; p.top_k = d.top_k; p.top_g = d.top_g;
   const int r = d.Hq / d.Hkv;
@@ -371,22 +381,22 @@ hipError_t run(const Dims& d, const void* Q, const float* cm, const float* gm, i
 }
 
 template <typename T, int D, int QB, int RW, int NSC>
-hipError_t run_g(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
-                 int32_t* gi, hipStream_t s) {
+hipError_t run_g(const Dims& d, const void* Q, const void* Qprev, int causal, const float* cm,
+                 const float* gm, int32_t* ci, int32_t* gi, hipStream_t s) {
   // 8 * top_k group candidates per row at most
-  if (d.top_k <= 8) return run<T, D, QB, RW, NSC, 1>(d, Q, cm, gm, ci, gi, s);
-  if (d.top_k <= 16) return run<T, D, QB, RW, NSC, 2>(d, Q, cm, gm, ci, gi, s);
-  if (d.top_k <= 32) return run<T, D, QB, RW, NSC, 4>(d, Q, cm, gm, ci, gi, s);
-  return run<T, D, QB, RW, NSC, 8>(d, Q, cm, gm, ci, gi, s);
+  if (d.top_k <= 8) return run<T, D, QB, RW, NSC, 1>(d, Q, Qprev, causal, cm, gm, ci, gi, s);
+  if (d.top_k <= 16) return run<T, D, QB, RW, NSC, 2>(d, Q, Qprev, causal, cm, gm, ci, gi, s);
+  if (d.top_k <= 32) return run<T, D, QB, RW, NSC, 4>(d, Q, Qprev, causal, cm, gm, ci, gi, s);
+  return run<T, D, QB, RW, NSC, 8>(d, Q, Qprev, causal, cm, gm, ci, gi, s);
 }
 
 template <typename T, int D, int QB, int RW>
-hipError_t run_c(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
-                 int32_t* gi, hipStream_t s) {
+hipError_t run_c(const Dims& d, const void* Q, const void* Qprev, int causal, const float* cm,
+                 const float* gm, int32_t* ci, int32_t* gi, hipStream_t s) {
   const int max_cand = (d.Skv - 1) / kChunk;   // chunks before the last query's own chunk
-  if (max_cand <= 256) return run_g<T, D, QB, RW, 4>(d, Q, cm, gm, ci, gi, s);
-  if (max_cand <= 1024) return run_g<T, D, QB, RW, 16>(d, Q, cm, gm, ci, gi, s);
-  return run_g<T, D, QB, RW, 32>(d, Q, cm, gm, ci, gi, s);
+  if (max_cand <= 256) return run_g<T, D, QB, RW, 4>(d, Q, Qprev, causal, cm, gm, ci, gi, s);
+  if (max_cand <= 1024) return run_g<T, D, QB, RW, 16>(d, Q, Qprev, causal, cm, gm, ci, gi, s);
+  return run_g<T, D, QB, RW, 32>(d, Q, Qprev, causal, cm, gm, ci, gi, s);
 }
 
 #ifndef HGA_ROUTE_ROWS_BLOCK
@@ -397,22 +407,23 @@ hipError_t run_c(const Dims& d, const void* Q, const float* cm, const float* gm,
 #endif
 
 template <typename T, int D>
-hipError_t run_d(const Dims& d, const void* Q, const float* cm, const float* gm, int32_t* ci,
-                 int32_t* gi, hipStream_t s) {
-  return d.Sq == 1 ? run_c<T, D, 1, HGA_ROUTE_ROWS_DECODE>(d, Q, cm, gm, ci, gi, s)
-                   : run_c<T, D, kChunk, HGA_ROUTE_ROWS_BLOCK>(d, Q, cm, gm, ci, gi, s);
+hipError_t run_d(const Dims& d, const void* Q, const void* Qprev, int causal, const float* cm,
+                 const float* gm, int32_t* ci, int32_t* gi, hipStream_t s) {
+  return d.Sq == 1 ? run_c<T, D, 1, HGA_ROUTE_ROWS_DECODE>(d, Q, Qprev, causal, cm, gm, ci, gi, s)
+                   : run_c<T, D, kChunk, HGA_ROUTE_ROWS_BLOCK>(d, Q, Qprev, causal, cm, gm, ci, gi, s);
 }
 
 }  // namespace
 
-hipError_t launch_route(const Dims& d, const void* Q, const float* chunk_mean,
-                        const float* group_mean, int32_t* chunk_idx, int32_t* group_idx,
-                        hipStream_t s) {
+hipError_t launch_route(const Dims& d, const void* Q, const void* Q_prev, bool causal,
+                        const float* chunk_mean, const float* group_mean, int32_t* chunk_idx,
+                        int32_t* group_idx, hipStream_t s) {
+  const int c = causal ? 1 : 0;
   if (d.bf16)
-    return d.D == 128 ? run_d<uint16_t, 128>(d, Q, chunk_mean, group_mean, chunk_idx, group_idx, s)
-                      : run_d<uint16_t, 64>(d, Q, chunk_mean, group_mean, chunk_idx, group_idx, s);
-  return d.D == 128 ? run_d<float, 128>(d, Q, chunk_mean, group_mean, chunk_idx, group_idx, s)
-                    : run_d<float, 64>(d, Q, chunk_mean, group_mean, chunk_idx, group_idx, s);
+    return d.D == 128 ? run_d<uint16_t, 128>(d, Q, Q_prev, c, chunk_mean, group_mean, chunk_idx, group_idx, s)
+                      : run_d<uint16_t, 64>(d, Q, Q_prev, c, chunk_mean, group_mean, chunk_idx, group_idx, s);
+  return d.D == 128 ? run_d<float, 128>(d, Q, Q_prev, c, chunk_mean, group_mean, chunk_idx, group_idx, s)
+                    : run_d<float, 64>(d, Q, Q_prev, c, chunk_mean, group_mean, chunk_idx, group_idx, s);
 }
 
 }  // namespace hga

@@ -25,6 +25,11 @@ the buffers.  The caller writes a segment's keys and values into
 ``k_history[:, :, i*S:(i+1)*S]`` (and the same for ``v_history``) before
 calling ``step(i, ...)``.
 
+With ``causal=True`` the routing is the strictly causal variant
+(``hga_route_causal``): block j of a segment is routed with the mean of the 64
+queries before it.  For a segment's first block those are the last 64 queries
+of the previous segment, which the runner keeps from the previous ``forward``.
+
 With ``kv_on_host=True`` the key/value history lives in pinned host memory
 (the page's RAM tier, same section): the summaries stay in GPU memory, and the
 kernels fetch only the rows they gather (the kept groups, the own chunk, the
@@ -32,10 +37,11 @@ segment's keys for its dK/dV) across the host link.
 """
 from __future__ import annotations
 
+import contextlib
 from dataclasses import dataclass
 
 from . import (CHUNK, hga_attend_bwd_dkdv_range, hga_attend_bwd_dq, hga_attend_bwd_workspace,
-               hga_attend_fwd, hga_build_summaries, hga_route, make_shape)
+               hga_attend_fwd, hga_build_summaries, hga_route, hga_route_causal, make_shape)
 
 
 @dataclass
@@ -51,7 +57,8 @@ class SegmentResult:
 class SegmentRunner:
     def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int,
                  seg_len: int, top_k: int, top_g: int, dtype: str = "bf16",
-                 softmax_scale: float = 0.0, device="cuda:0", kv_on_host: bool = False):
+                 softmax_scale: float = 0.0, device="cuda:0", kv_on_host: bool = False,
+                 causal: bool = False):
         import torch
         if seg_len % CHUNK or seq_len % seg_len:
             raise ValueError("seg_len must be a multiple of 64 dividing seq_len")
@@ -59,6 +66,7 @@ class SegmentRunner:
         self.L, self.S, self.top_k, self.top_g = seq_len, seg_len, top_k, top_g
         self.dtype, self.scale = dtype, softmax_scale
         self.nseg = seq_len // seg_len
+        self.causal = causal
         elt = torch.bfloat16 if dtype == "bf16" else torch.float32
         f32, i32 = torch.float32, torch.int32
         kv = (batch, n_kv_heads, seq_len, head_dim)
@@ -81,6 +89,9 @@ class SegmentRunner:
         self.dQ = torch.empty(q, dtype=elt, device=device)
         self.dK = torch.zeros(kv, dtype=elt, device=device)
         self.dV = torch.zeros(kv, dtype=elt, device=device)
+        # strictly causal routing: the last 64 queries of the previous segment
+        self.q_prev = torch.zeros(batch, n_q_heads, CHUNK, head_dim, dtype=elt, device=device) \
+            if causal else None
         # the last segment needs the largest workspace (longest history)
         self.workspace = torch.empty(hga_attend_bwd_workspace(self.shape(self.nseg - 1)),
                                      dtype=torch.uint8, device=device)
@@ -97,10 +108,19 @@ class SegmentRunner:
         c0, c1 = i * self.S // CHUNK, (i + 1) * self.S // CHUNK
         hga_build_summaries(s, self.k_history, self.chunk_mean, self.group_mean, c0, c1,
                             stream=stream)
-        hga_route(s, Q, self.chunk_mean, self.group_mean, self.chunk_idx, self.group_idx,
-                  stream=stream)
+        if self.causal:
+            hga_route_causal(s, Q, self.q_prev if i > 0 else None, self.chunk_mean,
+                             self.group_mean, self.chunk_idx, self.group_idx, stream=stream)
+        else:
+            hga_route(s, Q, self.chunk_mean, self.group_mean, self.chunk_idx, self.group_idx,
+                      stream=stream)
         hga_attend_fwd(s, Q, self.k_history, self.v_history, self.group_idx, self.O, self.lse,
                        stream=stream)
+        if self.causal:
+            # the next segment's first block routes with this segment's last 64 queries
+            import torch
+            with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
+                self.q_prev.copy_(Q[:, :, -CHUNK:])
 
     def backward(self, i: int, Q, dO, stream=None):
         """Step 4 for segment i, after forward(i, Q): dQ, and dK, dV of the

@@ -39,7 +39,7 @@ GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
-TAG_Q, TAG_K, TAG_V, TAG_DO, TAG_CENTROID, TAG_DUP = 1, 2, 3, 4, 5, 6
+TAG_Q, TAG_K, TAG_V, TAG_DO, TAG_CENTROID, TAG_DUP, TAG_QPREV = 1, 2, 3, 4, 5, 6, 7
 
 _BLOCK = 1 << 22  # draws per generation block (bounds temporary memory)
 
@@ -218,12 +218,14 @@ def _duplicate_chunks(Kr: np.ndarray, seed: int, fraction: float, dtype: str) ->
                         Kr[b, h, row, col] = np.nextafter(Kr[b, h, row, col], np.float32(np.inf))
 
 
-def make_inputs(w: Workload, with_grad_output: bool | None = None) -> dict:
+def make_inputs(w: Workload, with_grad_output: bool | None = None,
+                with_qprev: bool = False) -> dict:
     """Rounded inputs for a workload as numpy arrays.
 
     bf16 tensors are returned as uint16 bit patterns, fp32 tensors as float32.
-    Keys: Q [B,Hq,Sq,D], K and V [B,Hkv,Skv,D], and dO [B,Hq,Sq,D] when a
-    backward is wanted.
+    Keys: Q [B,Hq,Sq,D], K and V [B,Hkv,Skv,D], dO [B,Hq,Sq,D] when a backward
+    is wanted, and with ``with_qprev`` Qprev [B,Hq,64,D]: the 64 queries before
+    the segment (strictly causal routing), drawn like Q from their own stream.
     """
     B, Hq, Hkv, D, Sq, Skv = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.q_len, w.kv_len
     out = {}
@@ -246,6 +248,9 @@ def make_inputs(w: Workload, with_grad_output: bool | None = None) -> dict:
     out["K"] = K
     out["V"] = _round(normals(stream_state(w.seed, TAG_V), B * Hkv * Skv * D) * w.qv_scale,
                       w.dtype).reshape(B, Hkv, Skv, D)
+    if with_qprev:
+        out["Qprev"] = _round(normals(stream_state(w.seed, TAG_QPREV), B * Hq * 64 * D) *
+                              w.qv_scale, w.dtype).reshape(B, Hq, 64, D)
     if with_grad_output is None:
         with_grad_output = w.backward
     if with_grad_output:

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 3
+#define HGA_ABI_VERSION 4
 #define HGA_CHUNK 64      /* tokens per chunk (the page's 64-token chunks) */
 #define HGA_GROUP 8       /* tokens per group (the page's 8-token groups)  */
 #define HGA_QBLOCK 64     /* queries per routing block                      */
@@ -140,6 +140,22 @@ hga_status hga_build_summaries(const hga_shape* shape, const void* K, float* chu
 hga_status hga_route(const hga_shape* shape, const void* Q, const float* chunk_mean,
                      const float* group_mean, int32_t* chunk_idx, int32_t* group_idx,
                      void* stream);
+
+/* Strictly causal routing (page section "The one real caveat: causal leakage":
+ * a block's routing mixes its query positions, so earlier tokens learn about
+ * later ones; the page mentions a strictly causal variant without giving one).
+ * As hga_route, except that block j is routed with the mean of the 64 queries
+ * just before it: block j-1 of Q, or for the first block the 64 rows of
+ * Q_prev.  No position's key set then depends on a later position.
+ *   Q_prev     [B][Hq][64][D] dtype, the 64 queries before the segment
+ *              (positions kv_len-q_len-64 .. kv_len-q_len-1); required when
+ *              kv_len > q_len and top_k or top_g is non-zero, else not read
+ * The first block of a sequence (kv_len == q_len) has no candidate chunk and
+ * attends its own chunk only, as in hga_route.  Outputs as hga_route; the
+ * attention and backward calls take them unchanged. */
+hga_status hga_route_causal(const hga_shape* shape, const void* Q, const void* Q_prev,
+                            const float* chunk_mean, const float* group_mean,
+                            int32_t* chunk_idx, int32_t* group_idx, void* stream);
 
 /* Exact-token attention forward (page section "What HGA does differently":
  * attention runs on the exact tokens of the kept groups).  The query at

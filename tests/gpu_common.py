@@ -41,11 +41,13 @@ def run_forward(w: syn.Workload, x: dict | None = None):
     return s, x, t, out
 
 
-def check_routing(oracle, w, Qf, cm_o, gm_o, ci_gpu, gi_gpu, rows=None):
-    """GPU routing vs the oracle under the near-tie rule.  Returns the number of
-    rows where a near tie allowed a difference."""
+def check_routing(oracle, w, Qf, cm_o, gm_o, ci_gpu, gi_gpu, rows=None, causal=False,
+                  Qprev=None):
+    """GPU routing vs the oracle under the near-tie rule (``causal``: the
+    strictly causal variant, ``Qprev`` the 64 queries before the segment).
+    Returns the number of rows where a near tie allowed a difference."""
     ci_o, gi_o, cs, gs = oracle.route(Qf, cm_o, gm_o, w.kv_len, w.top_k, w.top_g,
-                                      want_scores=True)
+                                      want_scores=True, causal=causal, Qprev=Qprev)
     tolerated = 0
     forced = None
     B, Hq, nblk = ci_gpu.shape[:3]
@@ -61,7 +63,8 @@ def check_routing(oracle, w, Qf, cm_o, gm_o, ci_gpu, gi_gpu, rows=None):
     # groups: against the oracle's choice given the GPU's chunk sets
     if not np.array_equal(ci_gpu, ci_o):
         _, gi_o, _, gs = oracle.route(Qf, cm_o, gm_o, w.kv_len, w.top_k, w.top_g,
-                                      forced_chunk_idx=ci_gpu, want_scores=True)
+                                      forced_chunk_idx=ci_gpu, want_scores=True, causal=causal,
+                                      Qprev=Qprev)
     for idx in (rows if rows is not None else np.ndindex(B, Hq, nblk)):
         a, b = gi_gpu[idx], gi_o[idx]
         v = a[a >= 0]
