@@ -254,3 +254,14 @@ def test_decode_full_size_sampled_sequences(oracle):
     out = _run(w, x)
     tolerated = _check(oracle, w, x, out, batches=[0, 5, 10, 15])
     print(f"[routing] decode full size: rows inside the near-tie band: {tolerated}", flush=True)
+
+
+@pytest.mark.gpu
+def test_decode_maximum_cache(oracle):
+    """A full 131072-token cache (the largest decode shape): 2047 candidate
+    chunks, the widest decode routing select."""
+    w = _workload("max", 1, 4, 1, 128, 131072, 16, 64, "bf16", 44)
+    print("[case] decode maximum cache", flush=True)
+    x = syn.make_inputs(w)
+    out = _run(w, x)
+    _check(oracle, w, x, out)

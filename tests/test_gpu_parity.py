@@ -251,3 +251,30 @@ def test_full_size_backward_sampled_kv_group(oracle, name, b, hkv):
     assert_close(f64(dQ)[b:b + 1, hs], dQ_o, w.dtype, "dQ")
     assert_close(f64(dK)[b:b + 1, hkv:hkv + 1], dK_o, w.dtype, "dK")
     assert_close(f64(dV)[b:b + 1, hkv:hkv + 1], dV_o, w.dtype, "dV")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_maximum_kv_length(oracle, dtype):
+    """kv_len = HGA_MAX_KV_LEN (131072): 2047 candidate chunks for the last
+    block (the widest routing select), a group-mask map of 2048 chunks per
+    row, dK/dV over every chunk of the history.  Two 64-query blocks at the end
+    of the history, full parity."""
+    from gpu_common import assert_close
+    w = syn.Workload("max_kv", 1, 2, 1, 64, 128, 131072, 12, 40, dtype, 71,
+                     0.125 if dtype == "bf16" else 0.4, backward=True)
+    print(f"[case] maximum kv_len {dtype}", flush=True)
+    s, x, t, out = run_forward(w)
+    xf = _oracle_inputs(w, x)
+    cm_o, gm_o = oracle.summaries(xf["K"])
+    np.testing.assert_allclose(f64(out["chunk_mean"]), cm_o, atol=1e-5, rtol=1e-5)
+    ci, gi = out["chunk_idx"].cpu().numpy(), out["group_idx"].cpu().numpy()
+    check_routing(oracle, w, xf["Q"], cm_o, gm_o, ci, gi)
+    O_o, lse_o = oracle.attend_fwd(xf["Q"], xf["K"], xf["V"], gi)
+    assert_close(f64(out["O"]), O_o, dtype, "O")
+    dQ, dK, dV = hga.backward(s, t["Q"], t["K"], t["V"], out["O"], out["lse"], t["dO"],
+                              out["group_idx"])
+    torch.cuda.synchronize()
+    dQ_o, dK_o, dV_o = oracle.attend_bwd(xf["Q"], xf["K"], xf["V"], gi, xf["dO"])
+    assert_close(f64(dQ), dQ_o, dtype, "dQ")
+    assert_close(f64(dK), dK_o, dtype, "dK")
+    assert_close(f64(dV), dV_o, dtype, "dV")
