@@ -57,7 +57,7 @@ def source_hash(phase: str) -> str:
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="segment_2k_over_16k")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -73,8 +73,8 @@ def parse():
     ap.add_argument("--causal", action="store_true",
                     help="strictly causal routing (block j routed with the 64 queries before it)")
     ap.add_argument("--decode", action="store_true",
-                    help="decode mode: one new token per sequence over a 16,424-token cache, "
-                         "batch 16 (routing + attention per step)")
+                    help="decode mode: 64 new tokens per sequence (one block) over a 16K "
+                         "cache, batch 16; with --causal the block is routed once")
     return ap.parse_args()
 
 
@@ -320,64 +320,81 @@ def decode_work(w, kept_groups: int) -> dict:
     return {"decode_route": route, "decode_attend": attend}
 
 
-def cpu_baseline_decode(w, x, cm, gm, budget_s: float = 12.0):
-    """The CPU oracle's decode (routing and attention of every head in fp64,
-    summaries given), single thread, over the batch's sequences one after
-    another, repeated until `budget_s` seconds of work are done."""
+def cpu_baseline_decode(w, x, cm, gm, causal=False, budget_s: float = 12.0):
+    """The CPU oracle on the same decode work, single thread, one sequence at
+    a time, cycling over four of the batch's sequences until `budget_s`
+    seconds of work are done.  Block routing: one token's decode (routing over
+    the resident summaries and attention, fp64).  Strictly causal routing: one
+    block of 64 tokens (the block's routing once, then the attention of its
+    64 tokens, which equals the forward over the block)."""
     import oracle
     from hierarchical_routed_sparse_amd import synthetic as syn
     oracle.build(force=False)
     seqs = []
-    for b in range(w.batch):
-        seqs.append((syn.to_f64(x["Q"][b:b + 1, :, 0], w.dtype), syn.to_f64(x["K"][b:b + 1], w.dtype),
-                     syn.to_f64(x["V"][b:b + 1], w.dtype), cm[b:b + 1], gm[b:b + 1]))
-        if b >= 3:
-            break                      # conversion bounded: four sequences are cycled
-    done, dt = 0, 0.0
+    for b in range(min(4, w.batch)):
+        f = {k: syn.to_f64(v[b:b + 1], w.dtype) for k, v in x.items()}
+        seqs.append((f, cm[b:b + 1], gm[b:b + 1]))
+    done, toks, dt = 0, 0, 0.0
     while dt < budget_s:
-        Q, K, V, c, g = seqs[done % len(seqs)]
+        f, c, g = seqs[done % len(seqs)]
         t0 = time.perf_counter()
-        oracle.decode(Q, K, V, c, g, w.top_k, w.top_g)
+        if causal:
+            _, gi = oracle.route(f["Q"], c, g, f["K"].shape[2], w.top_k, w.top_g, causal=True,
+                                 Qprev=f["Qprev"])
+            oracle.attend_fwd(f["Q"], f["K"], f["V"], gi)
+            toks += f["Q"].shape[2]
+        else:
+            oracle.decode(f["Q"][:, :, 0], f["K"], f["V"], c, g, w.top_k, w.top_g)
+            toks += 1
         dt += time.perf_counter() - t0
         done += 1
+    what = ("blocks of 64 tokens (routing once, attention of every token)" if causal
+            else "single-token decode steps (routing over the resident summaries and attention)")
     return {
-        "value": done / dt,
+        "value": toks / dt,
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"{done} single-sequence decode steps (all {w.n_q_heads} query heads: routing "
-                   f"over the resident summaries and attention, fp64) cycling over "
-                   f"{len(seqs)} of the {w.batch} sequences, {dt:.1f} s single-threaded"),
+        "sample": (f"{done} single-sequence {what}, all {w.n_q_heads} query heads, fp64, "
+                   f"cycling over {len(seqs)} of the {w.batch} sequences, {dt:.1f} s "
+                   f"single-threaded"),
     }
 
 
 def decode_main(args):
-    """Decode step of one layer: one new token for each of 16 sequences at
-    position 16423 of a 16,424-token cache (capacity 16,448); summaries of the
-    256 complete chunks resident (a decoder appends one chunk's summary every
-    64 tokens, outside this step).  Step = routing + attention, timed per kernel
-    with HIP events on the launch stream."""
+    """Decode of one layer: 64 consecutive new tokens (positions 16384-16447,
+    one block) for each of 16 sequences over a cache of capacity 16448; the
+    summaries of the 256 complete chunks before the block are resident (a
+    decoder appends one chunk's summary every 64 tokens).  Block routing: each
+    token is routed with its own query, then attended (2 kernels per token).
+    With --causal (strictly causal routing): the block is routed once from the
+    previous block's 64 queries, then each token is attended (1 kernel per
+    token).  The 64 steps are captured as one graph; a step is one token per
+    sequence.  The roofline kernel is the attention at position 16423."""
     import numpy as np
     import torch
     import hierarchical_routed_sparse_amd as hga
     from hierarchical_routed_sparse_amd import synthetic as syn
 
-    w = syn.WORKLOADS["decode_b16_16k"]
-    x = syn.make_inputs(w)
+    w = syn.WORKLOADS["decode_b16_16k"]            # kv_len 16424: the roofline position
+    T, j = 64, 256                                  # tokens 64j .. 64j + 63
+    cap = 64 * (j + 1)
+    wi = syn.scaled_workload(w, q_len=T, kv_len=cap)
+    x = syn.make_inputs(wi, with_qprev=args.causal)  # Q: the 64 tokens' queries
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    B, Hq, Hkv, D, L = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.kv_len
-    cap = -(-L // 64) * 64
-    s = hga.make_shape(B, Hq, Hkv, D, 1, L, w.top_k, w.top_g, dtype=w.dtype, kv_capacity=cap)
+    B, Hq, Hkv, D = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    shapes = [hga.make_shape(B, Hq, Hkv, D, 1, 64 * j + t + 1, w.top_k, w.top_g,
+                             dtype=w.dtype, kv_capacity=cap) for t in range(T)]
     edt = torch.bfloat16
-    K = torch.zeros(B, Hkv, cap, D, dtype=edt, device=dev)
-    V = torch.zeros(B, Hkv, cap, D, dtype=edt, device=dev)
-    K[:, :, :L] = syn.to_torch(x["K"], w.dtype, dev)
-    V[:, :, :L] = syn.to_torch(x["V"], w.dtype, dev)
-    Q = syn.to_torch(x["Q"], w.dtype, dev)[:, :, 0].contiguous()
+    K = syn.to_torch(x["K"], w.dtype, dev)
+    V = syn.to_torch(x["V"], w.dtype, dev)
+    Qt = syn.to_torch(x["Q"], w.dtype, dev)
+    Qs = [Qt[:, :, t].contiguous() for t in range(T)]
+    Qprev = syn.to_torch(x["Qprev"], w.dtype, dev) if args.causal else None
     cm = torch.zeros(B, Hkv, cap // 64, D, device=dev)
     gm = torch.zeros(B, Hkv, cap // 8, D, device=dev)
-    hga.hga_build_summaries(s, K, cm, gm, 0, L // 64)
+    hga.hga_build_summaries(shapes[0], K, cm, gm, 0, j)
     if args.host_kv:
         torch.cuda.synchronize()
         Kh = torch.empty(K.shape, dtype=edt, pin_memory=True)
@@ -392,55 +409,90 @@ def decode_main(args):
     # host-resident K/V: pass their GPU addresses (resolved once, outside any capture)
     Ka, Va = (hga._ptr(K, "K", host_ok=True), hga._ptr(V, "V", host_ok=True)) if args.host_kv \
         else (K, V)
-    phases = ["decode_route", "decode_attend"]
-    calls = {"decode_route": lambda: hga.hga_decode_route(s, Q, cm, gm, ci, gi),
-             "decode_attend": lambda: hga.hga_decode_attend(s, Q, Ka, Va, gi, O, lse)}
 
-    def step(ev=None):
+    def route(t):
+        if args.causal:
+            hga.hga_decode_route_causal(shapes[0], Qprev, cm, gm, ci, gi)
+        else:
+            hga.hga_decode_route(shapes[t], Qs[t], cm, gm, ci, gi)
+
+    def attend(t):
+        hga.hga_decode_attend(shapes[t], Qs[t], Ka, Va, gi, O, lse)
+
+    def block(acc=None):
+        # acc: [route_ms, attend_ms] accumulated from HIP events (eager pass)
         stream = torch.cuda.current_stream()
-        for i, p in enumerate(phases):
-            if ev: ev[i].record(stream)
-            calls[p]()
-        if ev: ev[len(phases)].record(stream)
+        for t in range(T):
+            if acc is not None:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record(stream)
+            if t == 0 or not args.causal:
+                route(t)
+            if acc is not None:
+                e[1].record(stream)
+            attend(t)
+            if acc is not None:
+                e[2].record(stream)
+                acc.append(e)
 
     for _ in range(args.warmup):
-        step()
+        block()
     torch.cuda.synchronize()
     if args.calibrate_copy:
         calibration_copy(dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    nblocks = max(1, -(-args.steps // T))   # whole blocks of 64 steps
+    evs = []
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
+    for _ in range(nblocks):
+        block(evs)
     torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    # the timed region: the step replayed from a HIP graph (a serving loop's form)
-    ms_step = timed_replays(graph_of(step), args.steps, args.warmup)
+    eager_ms = (time.perf_counter() - t0) * 1e3 / (nblocks * T)
+    route_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / (nblocks * T)
+    attend_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / (nblocks * T)
+    # the timed region: blocks of 64 steps replayed from a HIP graph
+    ms_step = timed_replays(graph_of(block), nblocks, 1) / T
+
+    # roofline kernel: the attention at position 16423 (token 39 of the block)
+    tr = 39
+    route(tr)
+    torch.cuda.synchronize()
     kept = int((gi >= 0).sum().item())
     work = decode_work(w, kept)
     rep = {}
-    for p in phases:
-        us = kernel_us(calls[p])
+    for p, fn in (("decode_route", lambda: route(tr)), ("decode_attend", lambda: attend(tr))):
+        us = kernel_us(fn)
         ach = work[p] / (us * 1e-6) / 1e9
-        rep[p] = {"us": round(us, 2), "bound": "hbm",
+        rep[p] = {"kernel_us": round(us, 2), "bound": "hbm",
                   "algorithmic_bytes": work[p], "achieved_GBs": round(ach, 1),
                   "frac": round(ach / PEAK_HBM_GBS, 4)}
+    rep["decode_route"]["us_per_token_in_step"] = round(route_ms * 1e3, 2)
+    rep["decode_attend"]["us_per_token_in_step"] = round(attend_ms * 1e3, 2)
     dom = "decode_attend"
-    ach = work[dom] / (rep[dom]["us"] * 1e-6) / 1e9
+    us = rep[dom]["kernel_us"]
+    ach = work[dom] / (us * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": ach / PEAK_HBM_GBS, "traffic": None if args.host_kv else load_traffic(dom),
-            "kernel": dom, "kernel_us": rep[dom]["us"], "algorithmic_per_launch": work[dom]}
+            "kernel": dom, "kernel_us": us, "algorithmic_per_launch": work[dom]}
     base = None
     if not args.no_cpu_baseline:
-        base = cpu_baseline_decode(w, x, cm.cpu().numpy().astype(np.float64),
-                                   gm.cpu().numpy().astype(np.float64))
+        cmh = cm.cpu().numpy().astype(np.float64)
+        gmh = gm.cpu().numpy().astype(np.float64)
+        if args.causal:
+            base = cpu_baseline_decode(wi, x, cmh, gmh, causal=True)
+        else:
+            xd = {"Q": x["Q"][:, :, tr:tr + 1], "K": x["K"][:, :, :w.kv_len],
+                  "V": x["V"][:, :, :w.kv_len]}
+            base = cpu_baseline_decode(w, xd, cmh[:, :, :w.kv_len // 64],
+                                       gmh[:, :, :8 * (w.kv_len // 64)])
+    form = "strictly causal routing, routed once per 64-token block" if args.causal \
+        else "each token routed with its own query"
     out = {
-        "metric": "HGA decode tokens/sec at 16K ctx (one new token per sequence, batch 16"
+        "metric": "HGA decode tokens/sec at 16K ctx (batch 16, " + form
                   + (", K/V in pinned host memory" if args.host_kv else "") + "), 1 MI355X",
         "value": B / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": nblocks * T,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
         "eager_ms_per_step": eager_ms,
@@ -449,10 +501,11 @@ def decode_main(args):
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded clustered keys, N(0,1)/sqrt(128) queries and values)",
-        "config": {"workload": f"{w.name}: decode at position {L - 1}, cache capacity {cap}",
-                   "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "kv_len": L,
+        "config": {"workload": f"{w.name}: 64 decode steps per sequence at positions "
+                               f"{64 * j}-{64 * j + T - 1}, cache capacity {cap}, {form}",
+                   "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
                    "chunk": 64, "group": 8, "top_k": w.top_k, "top_g": w.top_g,
-                   "kept_groups": kept},
+                   "kept_groups_at_16423": kept},
         "roofline": roof,
         "phases": rep,
         "cpu_baseline": base,

@@ -27,6 +27,7 @@ __all__ = [
     "hga_build_summaries", "hga_route", "hga_route_causal", "hga_attend_fwd", "hga_attend_bwd_workspace",
     "hga_attend_bwd", "hga_attend_bwd_dq", "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range",
     "hga_validate_decode_shape", "hga_decode", "hga_decode_route", "hga_decode_attend",
+    "hga_decode_route_causal",
     "forward", "backward", "decode",
 ]
 
@@ -98,8 +99,9 @@ def _load():
     lib.hga_decode.argtypes = [_SP] + [_vp] * 10
     lib.hga_decode_route.argtypes = [_SP] + [_vp] * 6
     lib.hga_decode_attend.argtypes = [_SP] + [_vp] * 7
+    lib.hga_decode_route_causal.argtypes = [_SP] + [_vp] * 6
     for name in ("hga_validate_shape", "hga_validate_decode_shape", "hga_decode", "hga_route_causal",
-                 "hga_decode_route", "hga_decode_attend", "hga_build_summaries", "hga_route", "hga_attend_fwd",
+                 "hga_decode_route", "hga_decode_attend", "hga_decode_route_causal", "hga_build_summaries", "hga_route", "hga_attend_fwd",
                  "hga_attend_bwd_workspace", "hga_attend_bwd", "hga_attend_bwd_dq",
                  "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range"):
         getattr(lib, name).restype = ctypes.c_int
@@ -370,6 +372,23 @@ def hga_decode_route(shape, Q, chunk_mean, group_mean, chunk_idx, group_idx, str
         _ptr(chunk_idx, "chunk_idx", torch.int32, sz["ci"], nullable=True),
         _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
         _stream(stream)), "hga_decode_route")
+
+
+def hga_decode_route_causal(shape, Q_prev, chunk_mean, group_mean, chunk_idx, group_idx,
+                            stream=None):
+    """Decode routing under strictly causal routing: once per block, from the
+    previous block's 64 queries Q_prev [B,Hq,64,D] (None in the first block)."""
+    import torch
+    sz, dt = _decode_sizes(shape)
+    _check(_load().hga_decode_route_causal(
+        ctypes.byref(shape),
+        _ptr(Q_prev, "Q_prev", dt, (shape.batch, shape.n_q_heads, QBLOCK, shape.head_dim),
+             nullable=True),
+        _ptr(chunk_mean, "chunk_mean", torch.float32, sz["cm"], nullable=True),
+        _ptr(group_mean, "group_mean", torch.float32, sz["gm"], nullable=True),
+        _ptr(chunk_idx, "chunk_idx", torch.int32, sz["ci"], nullable=True),
+        _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        _stream(stream)), "hga_decode_route_causal")
 
 
 def hga_decode_attend(shape, Q, K, V, group_idx, O, lse=None, stream=None):

@@ -253,6 +253,30 @@ hga_status hga_decode_route(const hga_shape* shape, const void* Q, const float* 
                                     (hipStream_t)stream));
 }
 
+hga_status hga_decode_route_causal(const hga_shape* shape, const void* Q_prev,
+                                   const float* chunk_mean, const float* group_mean,
+                                   int32_t* chunk_idx, int32_t* group_idx, void* stream) {
+  hga_status st = hga_validate_decode_shape(shape);
+  if (st != HGA_OK) return st;
+  if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
+  if (shape->top_k == 0 && shape->top_g == 0) return HGA_OK;
+  // the token's block j = (kv_len - 1) / 64: candidates are chunks 0..j-1
+  const int32_t j = (shape->kv_len - 1) / HGA_CHUNK;
+  if (j > 0 && (!Q_prev || !chunk_mean || (shape->top_g > 0 && !group_mean)))
+    return HGA_ERR_NULL;
+  // the block route over a one-block segment ending at the block's end: its
+  // only block is routed (strictly causal) with the mean of Q_prev
+  hga::Dims d = dims_of(shape);
+  d.Sq = HGA_QBLOCK;
+  d.Skv = (j + 1) * HGA_CHUNK;
+  d.q0 = j * HGA_CHUNK;
+  d.nblk = 1;
+  return from_hip(hga::launch_route(d, Q_prev, Q_prev, true, chunk_mean, group_mean,
+                                    shape->top_k > 0 ? chunk_idx : nullptr,
+                                    shape->top_g > 0 ? group_idx : nullptr,
+                                    (hipStream_t)stream));
+}
+
 hga_status hga_decode_attend(const hga_shape* shape, const void* Q, const void* K, const void* V,
                              const int32_t* group_idx, void* O, float* lse, void* stream) {
   hga_status st = hga_validate_decode_shape(shape);

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 4
+#define HGA_ABI_VERSION 5
 #define HGA_CHUNK 64      /* tokens per chunk (the page's 64-token chunks) */
 #define HGA_GROUP 8       /* tokens per group (the page's 8-token groups)  */
 #define HGA_QBLOCK 64     /* queries per routing block                      */
@@ -258,6 +258,22 @@ hga_status hga_decode_route(const hga_shape* shape, const void* Q, const float* 
                             void* stream);
 hga_status hga_decode_attend(const hga_shape* shape, const void* Q, const void* K, const void* V,
                              const int32_t* group_idx, void* O, float* lse, void* stream);
+
+/* Decode routing under strictly causal routing (see hga_route_causal): the
+ * token at position p = kv_len - 1 lies in block j = p / 64 and is routed with
+ * the mean of the 64 queries of block j - 1 (positions 64(j-1) .. 64j - 1),
+ * over the complete chunks before chunk j.  Neither depends on the position
+ * within the block, so the result serves every token of block j: a decoder
+ * calls this once when a block starts and hga_decode_attend for each token
+ * (with that token's own decode shape and the same group_idx).
+ *   Q_prev     [B][Hq][64][D] dtype, the 64 queries of block j - 1; not read
+ *              when j == 0 (the first block has no candidate chunk)
+ *   chunk_mean, group_mean   summaries of chunks 0 .. j-1 built
+ *   chunk_idx  [B][Hq][top_k] int32, nullable; group_idx [B][Hq][top_g]
+ * Same layouts and status codes as hga_decode_route. */
+hga_status hga_decode_route_causal(const hga_shape* shape, const void* Q_prev,
+                                   const float* chunk_mean, const float* group_mean,
+                                   int32_t* chunk_idx, int32_t* group_idx, void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert hga.hga_abi_version() == 4
+    assert hga.hga_abi_version() == 5
 
 
 def _ok_shape(**kw):

@@ -141,3 +141,67 @@ def test_route_causal_argument_errors():
     assert lib.hga_route_causal(ctypes.byref(bad), 16, 16, 16, 16, 16, 16, None) == 2
     dec = hga.make_shape(1, 32, 8, 128, 1, 1024, 16, 64)
     assert lib.hga_route_causal(ctypes.byref(dec), 16, 16, 16, 16, 16, 16, None) == 2
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("L0,k,g", [(16384 + 64 * 3, 16, 64), (640, 3, 11), (64, 2, 8)])
+def test_causal_decode_routes_once_per_block(oracle, L0, k, g):
+    """hga_decode_route_causal for block j = L0 / 64 equals the oracle's causal
+    routing of a one-block segment whose preceding queries are block j - 1;
+    every token of block j then attends with those groups exactly what the
+    oracle's attention gives its row of the block."""
+    import torch
+    from gpu_common import DEV, check_routing
+    j = L0 // 64
+    w = syn.Workload("cdec", 2, 8, 2, 128, 64, L0 + 64, k, g, "bf16", 66, 1 / math.sqrt(128))
+    x = syn.make_inputs(w, with_qprev=True)        # Q: block j, Qprev: block j - 1
+    cap = L0 + 64
+    K = syn.to_torch(x["K"], "bf16", DEV)
+    V = syn.to_torch(x["V"], "bf16", DEV)
+    cm = torch.full((2, 2, cap // 64, 128), float("nan"), device=DEV)
+    gm = torch.full((2, 2, cap // 8, 128), float("nan"), device=DEV)
+    s0 = hga.make_shape(2, 8, 2, 128, 1, L0 + 1, k, g, kv_capacity=cap)
+    hga.hga_build_summaries(s0, K, cm, gm, 0, j)
+    ci = torch.full((2, 8, k), -7, dtype=torch.int32, device=DEV)
+    gi = torch.full((2, 8, g), -7, dtype=torch.int32, device=DEV)
+    Qp = syn.to_torch(x["Qprev"], "bf16", DEV) if j > 0 else None
+    hga.hga_decode_route_causal(s0, Qp, cm, gm, ci, gi)
+    torch.cuda.synchronize()
+    xf = {kk: syn.to_f64(v, "bf16") for kk, v in x.items()}
+    # the oracle's layout spans the segment's own chunk j too (never a candidate)
+    cm_o, gm_o = oracle.summaries(xf["K"][:, :, :64 * (j + 1)])
+    wb = syn.scaled_workload(w, kv_len=64 * (j + 1))
+    ci_n = ci.cpu().numpy()[:, :, None]
+    gi_n = gi.cpu().numpy()[:, :, None]
+    if j > 0:
+        check_routing(oracle, wb, xf["Q"], cm_o, gm_o, ci_n, gi_n, causal=True, Qprev=xf["Qprev"])
+    else:
+        assert (ci_n == -1).all() and (gi_n == -1).all()
+    # every token of the block, attended with the block's groups
+    O_o, lse_o = oracle.attend_fwd(xf["Q"], xf["K"][:, :, :64 * (j + 1)],
+                                   xf["V"][:, :, :64 * (j + 1)], gi_n)
+    Qt = syn.to_torch(x["Q"], "bf16", DEV)
+    for i in (0, 17, 63):
+        s = hga.make_shape(2, 8, 2, 128, 1, 64 * j + i + 1, k, g, kv_capacity=cap)
+        O = torch.empty(2, 8, 128, dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty(2, 8, device=DEV)
+        hga.hga_decode_attend(s, Qt[:, :, i].contiguous(), K, V, gi, O, lse)
+        torch.cuda.synchronize()
+        got = O.float().cpu().numpy().astype(np.float64)
+        ref = O_o[:, :, i]
+        assert (np.abs(got - ref) <= 2e-2 + 1e-2 * np.abs(ref)).all(), i
+        assert np.allclose(lse.cpu().numpy(), lse_o[:, :, i], atol=2e-2, rtol=1e-2), i
+
+
+def test_decode_route_causal_argument_errors():
+    lib = ctypes.CDLL(hga.lib_path())
+    lib.hga_decode_route_causal.restype = ctypes.c_int
+    lib.hga_decode_route_causal.argtypes = [ctypes.POINTER(hga.HgaShape)] + [ctypes.c_void_p] * 6
+    s = hga.make_shape(4, 32, 8, 128, 1, 16424, 16, 64, kv_capacity=16448)
+    assert lib.hga_decode_route_causal(ctypes.byref(s), None, 16, 16, 16, 16, None) == 1  # Q_prev
+    assert lib.hga_decode_route_causal(ctypes.byref(s), 16, 16, 16, 16, None, None) == 1  # group_idx
+    assert lib.hga_decode_route_causal(ctypes.byref(s), 16, None, 16, 16, 16, None) == 1  # summaries
+    blk = hga.make_shape(4, 32, 8, 128, 64, 16384, 16, 64)
+    assert lib.hga_decode_route_causal(ctypes.byref(blk), 16, 16, 16, 16, 16, None) == 2
