@@ -327,6 +327,132 @@ void attend_bwd_dq_kernel(const DqP p) {
 
 // ============================================================== dK, dV
 
+// Work order of the dK/dV workgroups of one (b, kv head): its chunks sorted by
+// the number of routing rows that attend them (the workgroup's entries),
+// heaviest first.  A workgroup's time is a fixed part plus a part per entry,
+// and the entries per chunk vary about threefold; started in chunk order, a
+// heavy chunk dispatched late finishes long after the rest (longest-first
+// scheduling bounds that tail).  The order changes no result: every
+// workgroup owns its chunk's keys.  Counts above 255 share one bucket; order
+// within a bucket is the order of arrival.
+// 16 wavefronts per ordering workgroup: the map rows are spread over them,
+// and their loads are in flight together.
+constexpr int kOrderWaves = 16;
+constexpr int kOrderThreads = 64 * kOrderWaves;
+
+// Entries of chunks c0 .. c0+3 from routing rows rs, rs + 16, ... of one kv
+// head (rows of the head's query-head group, head-major, so consecutive in
+// the map from mrow0): rows whose own chunk it is, plus rows of later blocks
+// whose group-mask byte for it is non-zero.  rs is wave-uniform, so every
+// row quantity is scalar.  Batches of 8 rows: every load of a batch is issued
+// before the first use (rows past the end re-read row 0 and count nothing).
+// VEC: one 32-bit load per row (map rows and c0 4-byte aligned).
+template <bool VEC>
+__device__ __forceinline__ void count_quad(const DkvP& p, const uint8_t* mrow0, int rs, int nrows,
+                                           int c0, int own0, int (&n)[4]) {
+  constexpr int kBatch = 8;
+  // blk = rr % nblk advances by kOrderWaves % nblk (< nblk) per row step:
+  // one conditional subtraction keeps it reduced
+  const int step = kOrderWaves % p.nblk;
+  int blk = rs % p.nblk;
+  const long long rstride = (long long)kOrderWaves * p.nchunks;
+  const uint8_t* mrow = mrow0 + (long long)rs * p.nchunks;
+  for (int rr0 = rs; rr0 < nrows; rr0 += kOrderWaves * kBatch) {
+    uint32_t wd[kBatch];
+    int ownv[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const bool ok = rr0 + kOrderWaves * k < nrows;
+      ownv[k] = ok ? own0 + blk : -1;   // -1: below every chunk, counts nothing
+      const uint8_t* m = ok ? mrow : mrow0;
+      mrow += rstride;
+      blk += step;
+      blk -= blk >= p.nblk ? p.nblk : 0;
+      if constexpr (VEC) {
+        wd[k] = *reinterpret_cast<const uint32_t*>(m + c0);
+      } else {
+        uint32_t x = 0;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          x |= (uint32_t)m[c0 + kk < p.nchunks ? c0 + kk : c0] << (8 * kk);
+        wd[k] = x;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int c = c0 + kk;
+        n[kk] += ownv[k] == c ? 1 : (ownv[k] > c && ((wd[k] >> (8 * kk)) & 0xFFu) != 0) ? 1 : 0;
+      }
+  }
+}
+
+__global__ __launch_bounds__(kOrderThreads) void dkdv_order_kernel(const DkvP p, int32_t* order) {
+  constexpr int kMaxRange = 2048;   // HGA_MAX_KV_LEN / 64
+  __shared__ int s_cnt[kMaxRange];
+  __shared__ int s_hist[256];
+  __shared__ int s_wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.x, b = bh / p.Hkv, hkv = bh % p.Hkv;
+  const int r = p.Hq / p.Hkv, nrows = r * p.nblk;
+  const int own0 = p.q0 / kChunk;   // own chunk of block 0
+  const uint8_t* mrow0 = p.cmask + ((long long)b * p.Hq + hkv * r) * p.nblk * p.nchunks;
+  for (int i = tid; i < kMaxRange; i += kOrderThreads) s_cnt[i] = 0;
+  if (tid < 256) s_hist[tid] = 0;
+  __syncthreads();
+  // entries of every chunk of the range.  Lane q of wavefront wv counts
+  // chunks 4q .. 4q+3 of a 256-chunk window over rows wv, wv + 16, ...
+  const bool vec = (p.nchunks & 3) == 0 && (p.chunk0 & 3) == 0;
+  for (int w0 = 0; w0 < p.nrange; w0 += 256) {
+    const int i0 = w0 + 4 * lane;         // first range index of the quad
+    if (i0 < p.nrange) {
+      const int c0 = p.chunk0 + i0;
+      int n[4] = {0, 0, 0, 0};
+      if (vec)
+        count_quad<true>(p, mrow0, wv, nrows, c0, own0, n);
+      else
+        count_quad<false>(p, mrow0, wv, nrows, c0, own0, n);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (i0 + k < p.nrange && n[k] != 0) atomicAdd(&s_cnt[i0 + k], n[k]);
+    }
+  }
+  __syncthreads();
+  // counting sort on 256 buckets (bucket 255 - min(count, 255)): histogram,
+  // exclusive prefix, then placement
+  for (int i = tid; i < p.nrange; i += kOrderThreads) {
+    const int n = s_cnt[i];
+    atomicAdd(&s_hist[255 - (n < 255 ? n : 255)], 1);
+  }
+  __syncthreads();
+  int v = 0, incl = 0;
+  if (tid < 256) {
+    v = s_hist[tid];
+    incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(incl, d);
+      if (lane >= d) incl += u;
+    }
+    if (lane == 63) s_wsum[wv] = incl;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    int base = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) base += k < wv ? s_wsum[k] : 0;
+    s_hist[tid] = base + incl - v;   // first slot of the bucket
+  }
+  __syncthreads();
+  for (int i = tid; i < p.nrange; i += kOrderThreads) {
+    const int n = s_cnt[i];
+    const int pos = atomicAdd(&s_hist[255 - (n < 255 ? n : 255)], 1);
+    order[bh * p.nrange + pos] = p.chunk0 + i;
+  }
+}
+
 template <typename T, int D, int S>
 __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p) {
   using RT = RowTile<T, D>;
@@ -345,7 +471,9 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
   const int l16 = lane & 15, g4 = lane >> 4;
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = w / p.nrange, c = p.chunk0 + w % p.nrange;
+  // work items of one (b, kv head) in the order the ordering kernel chose:
+  // chunks with the most entries first (see dkdv_order_kernel)
+  const int bh = w / p.nrange, c = p.order[bh * p.nrange + w % p.nrange];
   const int b = bh / p.Hkv, hkv = bh % p.Hkv;
   const int r = p.Hq / p.Hkv;
   const int nrows = r * p.nblk;          // (query head in group, block), head-major
@@ -553,7 +681,8 @@ hipError_t run_dq(const Dims& d, const void* Q, const void* K, const void* V, co
 template <typename T, int D>
 hipError_t run_dkdv(const Dims& d, const void* Q, const void* K, const void* V, const float* lse,
                     const void* dO, const int32_t* gi, const float* delta, const uint8_t* cmask,
-                    void* dK, void* dV, int chunk_begin, int chunk_end, hipStream_t s) {
+                    int32_t* order, void* dK, void* dV, int chunk_begin, int chunk_end,
+                    hipStream_t s) {
   DkvP p;
   p.Q = Q; p.K = K; p.V = V; p.lse = lse; p.dO = dO; p.gidx = gi; p.delta = delta;
   p.cmask = cmask;
@@ -564,10 +693,12 @@ hipError_t run_dkdv(const Dims& d, const void* Q, const void* K, const void* V, 
   p.chunk0 = chunk_begin;
   p.nrange = chunk_end - chunk_begin;
   p.nwork = d.B * d.Hkv * p.nrange;
+  p.order = order;
   constexpr int kStageBytes = 2 * 64 * D * (int)sizeof(T) + 512;
   constexpr int S0 = HGA_DKV_STAGES;
   constexpr int S = S0 * kStageBytes <= 140 * 1024 ? S0 : (140 * 1024) / kStageBytes;
   static_assert(S >= 2, "at least two stages");
+  dkdv_order_kernel<<<d.B * d.Hkv, kOrderThreads, 0, s>>>(p, order);
   attend_bwd_dkdv_kernel<T, D, S><<<p.nwork, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
@@ -587,13 +718,14 @@ hipError_t launch_attend_bwd_dq(const Dims& d, const void* Q, const void* K, con
 
 hipError_t launch_attend_bwd_dkdv(const Dims& d, const void* Q, const void* K, const void* V,
                                   const float* lse, const void* dO, const int32_t* group_idx,
-                                  const float* delta, const uint8_t* cmask, void* dK, void* dV,
-                                  int chunk_begin, int chunk_end, hipStream_t s) {
+                                  const float* delta, const uint8_t* cmask, int32_t* order,
+                                  void* dK, void* dV, int chunk_begin, int chunk_end,
+                                  hipStream_t s) {
   if (d.bf16)
-    return d.D == 128 ? run_dkdv<uint16_t, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, chunk_begin, chunk_end, s)
-                      : run_dkdv<uint16_t, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, chunk_begin, chunk_end, s);
-  return d.D == 128 ? run_dkdv<float, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, chunk_begin, chunk_end, s)
-                    : run_dkdv<float, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, dK, dV, chunk_begin, chunk_end, s);
+    return d.D == 128 ? run_dkdv<uint16_t, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, order, dK, dV, chunk_begin, chunk_end, s)
+                      : run_dkdv<uint16_t, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, order, dK, dV, chunk_begin, chunk_end, s);
+  return d.D == 128 ? run_dkdv<float, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, order, dK, dV, chunk_begin, chunk_end, s)
+                    : run_dkdv<float, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, order, dK, dV, chunk_begin, chunk_end, s);
 }
 
 }  // namespace hga

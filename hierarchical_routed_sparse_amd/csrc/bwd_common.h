@@ -18,6 +18,7 @@ struct DkvP {
   void* dV;
   int B, Hq, Hkv, Sq, Skv, Scap, q0, nblk, top_g, nchunks, nwork;
   int chunk0, nrange;   // the workgroups cover chunks [chunk0, chunk0 + nrange)
+  const int32_t* order; // [B * Hkv][nrange]: chunk of work item i of a (b, kv head)
   float scale;
 };
 

@@ -32,7 +32,7 @@ hga_status from_hip(hipError_t e) { return e == hipSuccess ? HGA_OK : HGA_ERR_HI
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // workspace: delta (fp32 per query row), then the group-mask map (one byte per
-// (routing row, chunk))
+// (routing row, chunk)), then the dK/dV work order (one int per (b, kv head, chunk))
 size_t delta_bytes(const hga_shape* s) {
   return round256((size_t)s->batch * s->n_q_heads * s->q_len * sizeof(float));
 }
@@ -40,7 +40,13 @@ size_t cmask_bytes(const hga_shape* s) {
   return round256((size_t)s->batch * s->n_q_heads * (s->q_len / HGA_QBLOCK) *
                   (s->kv_len / HGA_CHUNK));
 }
-size_t workspace_bytes(const hga_shape* s) { return delta_bytes(s) + cmask_bytes(s); }
+// the dK/dV work order: one int per (b, kv head, chunk)
+size_t order_bytes(const hga_shape* s) {
+  return round256((size_t)s->batch * s->n_kv_heads * (s->kv_len / HGA_CHUNK) * sizeof(int32_t));
+}
+size_t workspace_bytes(const hga_shape* s) {
+  return delta_bytes(s) + cmask_bytes(s) + order_bytes(s);
+}
 
 // Checks shared by block and decode shapes (everything but q_len, kv_len and
 // kv_capacity).
@@ -206,8 +212,9 @@ hga_status hga_attend_bwd_dkdv_range(const hga_shape* shape, const void* Q, cons
   if (chunk_end == chunk_begin) return HGA_OK;
   return from_hip(hga::launch_attend_bwd_dkdv(
       dims_of(shape), Q, K, V, lse, dO, group_idx, (const float*)workspace,
-      (const uint8_t*)workspace + delta_bytes(shape), dK, dV, chunk_begin, chunk_end,
-      (hipStream_t)stream));
+      (const uint8_t*)workspace + delta_bytes(shape),
+      (int32_t*)((uint8_t*)workspace + delta_bytes(shape) + cmask_bytes(shape)), dK, dV,
+      chunk_begin, chunk_end, (hipStream_t)stream));
 }
 
 hga_status hga_attend_bwd_dkdv(const hga_shape* shape, const void* Q, const void* K,

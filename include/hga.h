@@ -172,7 +172,9 @@ hga_status hga_attend_fwd(const hga_shape* shape, const void* Q, const void* K, 
 /* Workspace bytes needed by the backward calls: the fp32 row statistics
  * delta [B][Hq][q_len], then a byte map [B][Hq][q_len/64][kv_len/64] whose
  * entry (routing row, chunk c) holds the mask of the row's kept groups in
- * chunk c (bit t = group 8c + t), each part rounded up to 256 bytes. */
+ * chunk c (bit t = group 8c + t), then the int32 work order of the dK/dV
+ * workgroups [B][Hkv][kv_len/64] (each kv head's chunks, most attended
+ * first), each part rounded up to 256 bytes. */
 hga_status hga_attend_bwd_workspace(const hga_shape* shape, size_t* bytes);
 
 /* Backward through the exact-token attention with the routing held fixed
