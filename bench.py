@@ -40,6 +40,7 @@ KERNEL_SOURCES = {
     "attend_fwd": ["attend_fwd.hip"],
     "attend_bwd_dq": ["attend_bwd.hip"],
     "attend_bwd_dkdv": ["attend_bwd.hip"],
+    "attend_bwd_dkdv_order": ["attend_bwd.hip"],
     "decode_route": ["route.hip"],
     "decode_attend": ["decode.hip"],
 }
@@ -106,16 +107,35 @@ def attended_pairs(group_idx) -> int:
     return 64 * 8 * kept + rows * (64 * 65 // 2)
 
 
+# the kernels one call of a phase launches, in order (the dK/dV call first
+# orders its workgroups with a small kernel of its own)
+PHASE_KERNELS = {
+    "attend_bwd_dkdv": ["attend_bwd_dkdv_order", "attend_bwd_dkdv"],
+}
+KERNEL_NAMES = {
+    "summaries": "summaries_kernel", "route": "route_kernel", "attend_fwd": "attend_fwd_kernel",
+    "attend_bwd_dq": "attend_bwd_dq_kernel", "attend_bwd_dkdv": "attend_bwd_dkdv_kernel",
+    "attend_bwd_dkdv_order": "dkdv_order_kernel", "decode_route": "route_kernel",
+    "decode_attend": "decode_kernel",
+}
+
+
 def load_traffic(phase: str):
+    """HBM bytes per call of `phase`, summed over the kernels the call launches,
+    from the stored counter runs; None when any of them is missing or its
+    sources changed since."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    r = rec.get("kernels", {}).get(phase)
-    if not r or r.get("source_sha") != source_hash(phase):
-        return None
-    return r.get("hbm_bytes_per_launch")
+    total = 0.0
+    for k in PHASE_KERNELS.get(phase, [phase]):
+        r = rec.get("kernels", {}).get(k)
+        if not r or r.get("source_sha") != source_hash(k):
+            return None
+        total += r.get("hbm_bytes_per_launch")
+    return total
 
 
 def cpu_baseline(w, x, budget_s: float = 12.0, causal: bool = False):
@@ -619,6 +639,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = load_traffic(dom)
     roof["kernel"] = dom
+    roof["launches"] = " + ".join(KERNEL_NAMES[k] for k in PHASE_KERNELS.get(dom, [dom]))
     roof["kernel_us"] = round(dom_us, 2)
     roof["algorithmic_per_launch"] = amount
 
