@@ -84,8 +84,10 @@ __device__ __forceinline__ void select_best(const uint32_t (&key)[NS], int n, in
   // Once exactly kk keys are >= T the kept set is decided: every key >= T,
   // which the tie step below also yields (it keeps all keys equal to T).
   uint32_t T = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t trial = T | (1u << bit);
+  for (uint32_t bm = 0x80000000u; bm != 0; bm >>= 1) {
+    // wave-uniform: kept in a scalar register (the comparisons take it as
+    // their scalar operand)
+    const uint32_t trial = __builtin_amdgcn_readfirstlane(T | bm);
     int tot = 0;
     if constexpr (NS <= 8) {
 #pragma unroll
@@ -154,7 +156,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const RouteP p) {
   __shared__ int s_chunk[RW][kMaxTopK];
   __shared__ float s_gscore[RW][8 * kMaxTopK];
 
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  // the wavefront index as a wave-uniform value: the per-row branches below
+  // are then uniform, and the selection's threshold and bit loop stay scalar
+  const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // work: (b, hkv, block, set of query heads); sets of one kv head run on one XCD
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int r = p.Hq / p.Hkv;
