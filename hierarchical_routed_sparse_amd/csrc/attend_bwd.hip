@@ -47,7 +47,7 @@ constexpr int kMaxTopG = 512;
 // returns how many were kept.  Every thread of the workgroup must call it.
 __device__ __forceinline__ int load_routing_row(const int32_t* grow, int top_g, int cb,
                                                 int* s_glist, int* s_wsum) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   int nvalid = 0;
   for (int i0 = 0; i0 < top_g; i0 += kThreads) {
     const int i = i0 + tid;
@@ -113,7 +113,7 @@ void attend_bwd_dq_kernel(const DqP p) {
   __shared__ int s_glist[kMaxTopG];
   __shared__ int s_wsum[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
   __shared__ uint32_t s_ent[kRowsPerPass];
   __shared__ int s_wsum[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);

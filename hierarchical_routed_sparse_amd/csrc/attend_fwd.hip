@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
   __shared__ int s_glist[kMaxTopG];
   __shared__ int s_wsum[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
 
   // work item: (b, hkv)-major so that one kv head's work shares an XCD

@@ -38,7 +38,7 @@ __device__ __forceinline__ int build_entries(const DkvP& p, int b, int hkv, int 
                                              uint32_t* s_ent, int* s_wsum,
                                              uint32_t want = 0x1FFu) {
   constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = p.Hq / p.Hkv;
   const int nrows = r * p.nblk;
   const int blk_first = c - p.q0 / kChunk;   // rows with block >= this can touch chunk c
