@@ -107,11 +107,10 @@ def attended_pairs(group_idx) -> int:
     return 64 * 8 * kept + rows * (64 * 65 // 2)
 
 
-# the kernels one call of a phase launches, in order (the dK/dV call first
-# orders its workgroups with a small kernel of its own)
-PHASE_KERNELS = {
-    "attend_bwd_dkdv": ["attend_bwd_dkdv_order", "attend_bwd_dkdv"],
-}
+# the kernels one call of a phase launches, in order, where there are several
+# (none at present: the dK/dV work order of the whole range is computed inside
+# the dQ call; only a chunk sub-range call adds dkdv_order_kernel)
+PHASE_KERNELS = {}
 KERNEL_NAMES = {
     "summaries": "summaries_kernel", "route": "route_kernel", "attend_fwd": "attend_fwd_kernel",
     "attend_bwd_dq": "attend_bwd_dq_kernel", "attend_bwd_dkdv": "attend_bwd_dkdv_kernel",

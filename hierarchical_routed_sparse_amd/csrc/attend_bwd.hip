@@ -82,9 +82,77 @@ struct DqP {
   void* dQ;
   float* delta;
   uint8_t* cmask;   // [routing row][chunk] kept-group masks, for the dK/dV kernel
-  int B, Hq, Hkv, Sq, Skv, Scap, q0, nblk, top_g, nwork;
+  int32_t* order;   // [B * Hkv][nchunks]: dK/dV work order (see dq_order_block)
+  int B, Hq, Hkv, Sq, Skv, Scap, q0, nblk, top_g, nwork, nchunks;
   float scale;
 };
+
+// The dK/dV work order of kv head bh = b * Hkv + hkv, computed by extra
+// workgroups at the end of the dQ grid (they start as dQ workgroups finish,
+// so the order costs no launch of its own): the chunks of the head sorted by
+// the number of routing rows that attend them, heaviest first (see
+// dkdv_order_kernel for why).  The counts come from the routing indices: a row
+// attends its own chunk and the chunks of its kept groups.
+template <int NT = kThreads>
+__device__ __forceinline__ void dq_order_block(const DqP& p, int bh, int* s_mem) {
+  constexpr int kMaxRange = 2048;   // HGA_MAX_KV_LEN / 64
+  constexpr int kBatch = 16;
+  int* s_cnt = s_mem;
+  int* s_hist = s_mem + kMaxRange;
+  int* s_wsum = s_hist + 256;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = bh / p.Hkv, hkv = bh % p.Hkv;
+  const int r = p.Hq / p.Hkv, nrows = r * p.nblk;
+  for (int i = tid; i < p.nchunks; i += NT) s_cnt[i] = 0;
+  for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
+  __syncthreads();
+  for (int rr = tid; rr < nrows; rr += NT) {
+    const int hq = hkv * r + rr / p.nblk, blk = rr % p.nblk;
+    atomicAdd(&s_cnt[p.q0 / kChunk + blk], 1);   // the row's own chunk
+    const int32_t* g = p.gidx + (((long long)b * p.Hq + hq) * p.nblk + blk) * p.top_g;
+    int prev = -1;
+    for (int i0 = 0; i0 < p.top_g; i0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) v[k] = i0 + k < p.top_g ? g[i0 + k] : -1;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        // kept groups are ascending: a chunk's groups are consecutive entries
+        const int c = v[k] >= 0 ? v[k] >> 3 : -1;
+        if (c >= 0 && c != prev) atomicAdd(&s_cnt[c], 1);
+        prev = c >= 0 ? c : prev;
+      }
+    }
+  }
+  __syncthreads();
+  // counting sort on 256 buckets (bucket 255 - min(count, 255))
+  for (int i = tid; i < p.nchunks; i += NT) {
+    const int n = s_cnt[i];
+    atomicAdd(&s_hist[255 - (n < 255 ? n : 255)], 1);
+  }
+  __syncthreads();
+  static_assert(NT == 256, "one bucket per thread");
+  const int v = s_hist[tid];
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(incl, d);
+    if (lane >= d) incl += u;
+  }
+  if (lane == 63) s_wsum[wv] = incl;
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) base += k < wv ? s_wsum[k] : 0;
+  __syncthreads();
+  s_hist[tid] = base + incl - v;   // first slot of the bucket
+  __syncthreads();
+  for (int i = tid; i < p.nchunks; i += NT) {
+    const int n = s_cnt[i];
+    const int pos = atomicAdd(&s_hist[255 - (n < 255 ? n : 255)], 1);
+    p.order[(long long)bh * p.nchunks + pos] = i;
+  }
+}
 
 // bf16: the register budget is held to four wavefronts per SIMD (4
 // workgroups per CU, the most the LDS stages allow): the kernel is bound by
@@ -116,7 +184,13 @@ void attend_bwd_dq_kernel(const DqP p) {
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  // workgroups past the dQ work compute the dK/dV work order
+  static_assert(S * kStage >= (2048 + 256 + 4) * (int)sizeof(int), "order scratch in smem");
+  if ((int)blockIdx.x >= p.nwork) {
+    dq_order_block(p, (int)blockIdx.x - p.nwork, reinterpret_cast<int*>(smem));
+    return;
+  }
+  const int w = xcd_remap(blockIdx.x, p.nwork);
   const int r = p.Hq / p.Hkv;
   const int per_bh = r * p.nblk;
   const int bh = w / per_bh, rem = w % per_bh;
@@ -662,10 +736,11 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
 template <typename T, int D>
 hipError_t run_dq(const Dims& d, const void* Q, const void* K, const void* V, const void* O,
                   const float* lse, const void* dO, const int32_t* gi, void* dQ, float* delta,
-                  uint8_t* cmask, hipStream_t s) {
+                  uint8_t* cmask, int32_t* order, hipStream_t s) {
   DqP p;
   p.Q = Q; p.K = K; p.V = V; p.O = O; p.lse = lse; p.dO = dO; p.gidx = gi; p.dQ = dQ;
-  p.delta = delta; p.cmask = cmask;
+  p.delta = delta; p.cmask = cmask; p.order = order;
+  p.nchunks = d.Skv / kChunk;
   p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.Scap = d.Scap; p.q0 = d.q0;
   p.nblk = d.nblk; p.top_g = d.top_g; p.scale = d.scale;
   p.nwork = d.B * d.Hq * d.nblk;
@@ -674,15 +749,16 @@ hipError_t run_dq(const Dims& d, const void* Q, const void* K, const void* V, co
   constexpr int S0 = HGA_DQ_STAGES;
   constexpr int S = S0 * kStageBytes <= 128 * 1024 ? S0 : (128 * 1024) / kStageBytes;
   static_assert(S >= 2, "at least two stages");
-  attend_bwd_dq_kernel<T, D, TK, S><<<p.nwork, kThreads, 0, s>>>(p);
+  // + one workgroup per (b, kv head) for the dK/dV work order
+  attend_bwd_dq_kernel<T, D, TK, S><<<p.nwork + d.B * d.Hkv, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t run_dkdv(const Dims& d, const void* Q, const void* K, const void* V, const float* lse,
                     const void* dO, const int32_t* gi, const float* delta, const uint8_t* cmask,
-                    int32_t* order, void* dK, void* dV, int chunk_begin, int chunk_end,
-                    hipStream_t s) {
+                    int32_t* order, bool order_ready, void* dK, void* dV, int chunk_begin,
+                    int chunk_end, hipStream_t s) {
   DkvP p;
   p.Q = Q; p.K = K; p.V = V; p.lse = lse; p.dO = dO; p.gidx = gi; p.delta = delta;
   p.cmask = cmask;
@@ -698,7 +774,8 @@ hipError_t run_dkdv(const Dims& d, const void* Q, const void* K, const void* V, 
   constexpr int S0 = HGA_DKV_STAGES;
   constexpr int S = S0 * kStageBytes <= 140 * 1024 ? S0 : (140 * 1024) / kStageBytes;
   static_assert(S >= 2, "at least two stages");
-  dkdv_order_kernel<<<d.B * d.Hkv, kOrderThreads, 0, s>>>(p, order);
+  // the full range's order comes with the dQ workspace; a sub-range orders its own
+  if (!order_ready) dkdv_order_kernel<<<d.B * d.Hkv, kOrderThreads, 0, s>>>(p, order);
   attend_bwd_dkdv_kernel<T, D, S><<<p.nwork, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
@@ -708,24 +785,24 @@ hipError_t run_dkdv(const Dims& d, const void* Q, const void* K, const void* V, 
 hipError_t launch_attend_bwd_dq(const Dims& d, const void* Q, const void* K, const void* V,
                                 const void* O, const float* lse, const void* dO,
                                 const int32_t* group_idx, void* dQ, float* delta,
-                                uint8_t* cmask, hipStream_t s) {
+                                uint8_t* cmask, int32_t* order, hipStream_t s) {
   if (d.bf16)
-    return d.D == 128 ? run_dq<uint16_t, 128>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, s)
-                      : run_dq<uint16_t, 64>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, s);
-  return d.D == 128 ? run_dq<float, 128>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, s)
-                    : run_dq<float, 64>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, s);
+    return d.D == 128 ? run_dq<uint16_t, 128>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, order, s)
+                      : run_dq<uint16_t, 64>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, order, s);
+  return d.D == 128 ? run_dq<float, 128>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, order, s)
+                    : run_dq<float, 64>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, order, s);
 }
 
 hipError_t launch_attend_bwd_dkdv(const Dims& d, const void* Q, const void* K, const void* V,
                                   const float* lse, const void* dO, const int32_t* group_idx,
                                   const float* delta, const uint8_t* cmask, int32_t* order,
-                                  void* dK, void* dV, int chunk_begin, int chunk_end,
-                                  hipStream_t s) {
+                                  bool order_ready, void* dK, void* dV, int chunk_begin,
+                                  int chunk_end, hipStream_t s) {
   if (d.bf16)
-    return d.D == 128 ? run_dkdv<uint16_t, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, order, dK, dV, chunk_begin, chunk_end, s)
-                      : run_dkdv<uint16_t, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, order, dK, dV, chunk_begin, chunk_end, s);
-  return d.D == 128 ? run_dkdv<float, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, order, dK, dV, chunk_begin, chunk_end, s)
-                    : run_dkdv<float, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, order, dK, dV, chunk_begin, chunk_end, s);
+    return d.D == 128 ? run_dkdv<uint16_t, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, order, order_ready, dK, dV, chunk_begin, chunk_end, s)
+                      : run_dkdv<uint16_t, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, order, order_ready, dK, dV, chunk_begin, chunk_end, s);
+  return d.D == 128 ? run_dkdv<float, 128>(d, Q, K, V, lse, dO, group_idx, delta, cmask, order, order_ready, dK, dV, chunk_begin, chunk_end, s)
+                    : run_dkdv<float, 64>(d, Q, K, V, lse, dO, group_idx, delta, cmask, order, order_ready, dK, dV, chunk_begin, chunk_end, s);
 }
 
 }  // namespace hga

@@ -32,7 +32,9 @@ hga_status from_hip(hipError_t e) { return e == hipSuccess ? HGA_OK : HGA_ERR_HI
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // workspace: delta (fp32 per query row), then the group-mask map (one byte per
-// (routing row, chunk)), then the dK/dV work order (one int per (b, kv head, chunk))
+// (routing row, chunk)), then two dK/dV work orders (one int per (b, kv head,
+// chunk) each): the full range's, written by the dQ call, and a sub-range's,
+// written by the range call itself (so a range call never spoils the other)
 size_t delta_bytes(const hga_shape* s) {
   return round256((size_t)s->batch * s->n_q_heads * s->q_len * sizeof(float));
 }
@@ -45,7 +47,13 @@ size_t order_bytes(const hga_shape* s) {
   return round256((size_t)s->batch * s->n_kv_heads * (s->kv_len / HGA_CHUNK) * sizeof(int32_t));
 }
 size_t workspace_bytes(const hga_shape* s) {
-  return delta_bytes(s) + cmask_bytes(s) + order_bytes(s);
+  return delta_bytes(s) + cmask_bytes(s) + 2 * order_bytes(s);
+}
+int32_t* order_full(const hga_shape* s, void* ws) {
+  return (int32_t*)((uint8_t*)ws + delta_bytes(s) + cmask_bytes(s));
+}
+int32_t* order_range(const hga_shape* s, void* ws) {
+  return (int32_t*)((uint8_t*)ws + delta_bytes(s) + cmask_bytes(s) + order_bytes(s));
 }
 
 // Checks shared by block and decode shapes (everything but q_len, kv_len and
@@ -194,7 +202,8 @@ hga_status hga_attend_bwd_dq(const hga_shape* shape, const void* Q, const void* 
   if (!workspace || workspace_bytes < ::workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
   return from_hip(hga::launch_attend_bwd_dq(
       dims_of(shape), Q, K, V, O, lse, dO, group_idx, dQ, (float*)workspace,
-      (uint8_t*)workspace + delta_bytes(shape), (hipStream_t)stream));
+      (uint8_t*)workspace + delta_bytes(shape), order_full(shape, workspace),
+      (hipStream_t)stream));
 }
 
 hga_status hga_attend_bwd_dkdv_range(const hga_shape* shape, const void* Q, const void* K,
@@ -210,10 +219,12 @@ hga_status hga_attend_bwd_dkdv_range(const hga_shape* shape, const void* Q, cons
   if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > shape->kv_len / HGA_CHUNK)
     return HGA_ERR_SHAPE;
   if (chunk_end == chunk_begin) return HGA_OK;
+  // the whole range uses the work order the dQ call wrote; a sub-range orders itself
+  const bool full = chunk_begin == 0 && chunk_end == shape->kv_len / HGA_CHUNK;
   return from_hip(hga::launch_attend_bwd_dkdv(
       dims_of(shape), Q, K, V, lse, dO, group_idx, (const float*)workspace,
       (const uint8_t*)workspace + delta_bytes(shape),
-      (int32_t*)((uint8_t*)workspace + delta_bytes(shape) + cmask_bytes(shape)), dK, dV,
+      full ? order_full(shape, workspace) : order_range(shape, workspace), full, dK, dV,
       chunk_begin, chunk_end, (hipStream_t)stream));
 }
 

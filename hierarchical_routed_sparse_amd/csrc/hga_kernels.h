@@ -31,13 +31,13 @@ hipError_t launch_attend_fwd(const Dims& d, const void* Q, const void* K, const 
 hipError_t launch_attend_bwd_dq(const Dims& d, const void* Q, const void* K, const void* V,
                                 const void* O, const float* lse, const void* dO,
                                 const int32_t* group_idx, void* dQ, float* delta,
-                                uint8_t* cmask, hipStream_t s);
+                                uint8_t* cmask, int32_t* order, hipStream_t s);
 
 hipError_t launch_attend_bwd_dkdv(const Dims& d, const void* Q, const void* K, const void* V,
                                   const float* lse, const void* dO, const int32_t* group_idx,
                                   const float* delta, const uint8_t* cmask, int32_t* order,
-                                  void* dK, void* dV, int chunk_begin, int chunk_end,
-                                  hipStream_t s);
+                                  bool order_ready, void* dK, void* dV, int chunk_begin,
+                                  int chunk_end, hipStream_t s);
 
 // Decode attention (one query per (b, hq) at position Skv - 1; d.Sq == 1).
 hipError_t launch_decode_attend(const Dims& d, const void* Q, const void* K, const void* V,

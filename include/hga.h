@@ -172,9 +172,11 @@ hga_status hga_attend_fwd(const hga_shape* shape, const void* Q, const void* K, 
 /* Workspace bytes needed by the backward calls: the fp32 row statistics
  * delta [B][Hq][q_len], then a byte map [B][Hq][q_len/64][kv_len/64] whose
  * entry (routing row, chunk c) holds the mask of the row's kept groups in
- * chunk c (bit t = group 8c + t), then the int32 work order of the dK/dV
+ * chunk c (bit t = group 8c + t), then two int32 work orders of the dK/dV
  * workgroups [B][Hkv][kv_len/64] (each kv head's chunks, most attended
- * first), each part rounded up to 256 bytes. */
+ * first): the whole range's, written by the dQ call, and a chunk sub-range's,
+ * written by hga_attend_bwd_dkdv_range itself.  Each part is rounded up to
+ * 256 bytes. */
 hga_status hga_attend_bwd_workspace(const hga_shape* shape, size_t* bytes);
 
 /* Backward through the exact-token attention with the routing held fixed
@@ -195,10 +197,11 @@ hga_status hga_attend_bwd(const hga_shape* shape, const void* Q, const void* K, 
 
 /* The two halves of hga_attend_bwd, for callers that schedule them apart.
  * hga_attend_bwd_dq computes dQ and writes the row statistics
- * delta = rowsum(dO * O) and the group-mask map into the workspace;
- * hga_attend_bwd_dkdv then reads both from the same workspace and computes
- * dK and dV.  The dkdv call must follow a dq call with the same inputs, on
- * the same stream (or after it has completed). */
+ * delta = rowsum(dO * O), the group-mask map and the dK/dV work order of the
+ * whole chunk range into the workspace; hga_attend_bwd_dkdv then reads them
+ * from the same workspace and computes dK and dV.  The dkdv call must follow
+ * a dq call with the same inputs, on the same stream (or after it has
+ * completed). */
 hga_status hga_attend_bwd_dq(const hga_shape* shape, const void* Q, const void* K,
                              const void* V, const void* O, const float* lse, const void* dO,
                              const int32_t* group_idx, void* dQ, void* workspace,

@@ -92,9 +92,9 @@ def test_null_and_workspace_errors_before_launch(lib):
     assert lib.hga_attend_bwd(ctypes.byref(s), *args[:10], None, need, None) == 4
     assert lib.hga_attend_bwd(ctypes.byref(s), *args, need - 1, None) == 4
     # the workspace holds delta, the one-byte-per-(routing row, chunk) group map
-    # and the dK/dV work order (one int per (b, kv head, chunk))
+    # and two dK/dV work orders (one int per (b, kv head, chunk) each)
     nblk, nch = 2048 // 64, 16384 // 64
-    assert need == 4 * 32 * 2048 + 32 * nblk * nch + 4 * 8 * nch
+    assert need == 4 * 32 * 2048 + 32 * nblk * nch + 2 * 4 * 8 * nch
     lib.hga_attend_bwd_dkdv_range.argtypes = ([SP] + [ctypes.c_void_p] * 6 + [ctypes.c_int32] * 2
                                               + [ctypes.c_void_p] * 3 + [ctypes.c_size_t,
                                                                          ctypes.c_void_p])
