@@ -574,16 +574,14 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
   }
   const float c2 = p.scale * kLog2e;
 
-  // loop-invariant per-lane offsets (see attend_fwd.hip)
-  // bf16: query rows in perm_row order (conflict-free transposing reads);
-  // fp32: natural order
-  using QRO = std::conditional_t<sizeof(T) == 2, RowOffsetsPerm<D>, RowOffsets<T, D>>;
-  QRO qro;
+  // loop-invariant per-lane offsets (see attend_fwd.hip); query rows in
+  // natural order: result item i of lane group g is query 4g + i of its
+  // 16-row slice, and the transposing reads cover rows 4g .. 4g + 3 (the tile
+  // swizzle keeps both read patterns conflict-free)
+  RowOffsets<T, D> qro;
   qro.init();
-  TrOffsetsPerm<(sizeof(T) == 2 ? D : 16)> qto;
+  TrOffsets<(sizeof(T) == 2 ? D : 16)> qto;
   if constexpr (sizeof(T) == 2) qto.init();
-  // query (within its 16-row slice) of result item i of this lane's group
-  auto qperm = [&](int i) { return sizeof(T) == 2 ? 4 * i + perm_sigma(g4) : 4 * g4 + i; };
   uint32_t ld_off[kIssues];
 #pragma unroll
   for (int j = 0; j < kIssues; ++j) {
@@ -660,17 +658,14 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
 #pragma unroll
         for (int qs = 0; qs < 4; ++qs) {
           // queries 16qs + 4g + i: stats of wave-slot qs at [lse 16 | delta 16]
-          float lq[4], dq[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            lq[i] = stat[32 * qs + qperm(i)];
-            dq[i] = stat[32 * qs + 16 + qperm(i)];
-          }
+          const float4 l4 = *reinterpret_cast<const float4*>(stat + 32 * qs + 4 * g4);
+          const float4 d4 = *reinterpret_cast<const float4*>(stat + 32 * qs + 16 + 4 * g4);
+          const float lq[4] = {l4.x, l4.y, l4.z, l4.w}, dq[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float nl = kvalid ? -lq[i] * kLog2e : -INFINITY;
             float pr = __builtin_amdgcn_exp2f(fmaf(sacc[qs][i], c2, nl));
-            if (local && kin > 16 * qs + qperm(i)) pr = 0.f;
+            if (local && kin > 16 * qs + 4 * g4 + i) pr = 0.f;
             sacc[qs][i] = pr;
             dpacc[qs][i] = pr * (dpacc[qs][i] - dq[i]);
           }
@@ -681,7 +676,7 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
         frag_from_acc(dsf[0], dpacc[0], dpacc[1]);
         frag_from_acc(dsf[1], dpacc[2], dpacc[3]);
         // dV^T += dO^T . P and dK^T += Q^T . dS; the transposed operands cover
-        // queries 32mm + qperm(t), 32mm + 16 + qperm(t) of column block cb
+        // queries 32mm + 4g + t, 32mm + 16 + 4g + t of column block cb
         if constexpr (sizeof(T) == 2) {
           uint32_t qa[D / 16];
 #pragma unroll

@@ -203,12 +203,11 @@ __device__ __forceinline__ void load_pair(Pair<float>& p, const float* row0, lon
 // {4-11, 16-19, 28-31} (and the same + 32); a pass is conflict-free when its
 // 16 lanes read 16 different 16-byte units of the 256-byte bank row.  A
 // ds_read_b64_tr_b16 is served per half-wave (32 lanes x 8 bytes).  The
-// swizzle row ^ (row odd ? 14 : 0) (row mod 16) makes every read pattern of
-// the attention kernels conflict-free under these rules: row operands in
-// natural row order (lane n: row n) and in the dK/dV kernel's permuted order
-// (perm_row), and transposing reads of 8 consecutive rows or of the permuted
-// rows 4e + sigma(g).  (The plain swizzle, unit ^ row, leaves the permuted
-// row reads and the consecutive-row transposing reads two-way conflicted.)
+// swizzle row ^ (row odd ? 14 : 0) (row mod 16) makes the read patterns of
+// the attention kernels conflict-free under these rules: row operands (lane
+// n of a 16-lane group: row n) and transposing reads of 8 consecutive rows.
+// (The plain swizzle, unit ^ row, leaves the transposing reads two-way
+// conflicted.)
 template <typename T, int D> struct RowTile {
   static constexpr int kUnits = D * Elem<T>::kBytes / 16;   // units per row
   static constexpr int kBytes = 64 * D * Elem<T>::kBytes;
@@ -552,47 +551,6 @@ __device__ __forceinline__ void tr_read8_sched(Frag<uint16_t> (&f)[4], const uin
     f[i].w[3] = (uint32_t)(uint16_t)y[2] | ((uint32_t)(uint16_t)y[3] << 16);
   }
 }
-
-// Row order within a 16-row slice used by the bf16 products whose results
-// feed a transposing read: operand row n holds element perm_row(n) =
-// 4(n % 4) + sigma(n / 4), sigma = (0, 2, 1, 3), so the 16x16 result item i of
-// lane group g is element 4i + sigma(g).  The transposing read that gathers
-// items 0..3 of lane group g then covers rows 4e + sigma(g), e = 0..3: a
-// half-wave reads 8 rows spaced 2 apart, which the row swizzle (RowTile::swz)
-// spreads over all 64 banks; consecutive rows would collide in pairs.
-__device__ __forceinline__ int perm_sigma(int g) { return ((g & 1) << 1) | (g >> 1); }
-__device__ __forceinline__ int perm_row(int n) { return 4 * (n & 3) + perm_sigma(n >> 2); }
-
-// RowOffsets for bf16 with the rows in perm_row order.
-template <int D>
-struct RowOffsetsPerm {
-  uint32_t o[D / 32];
-  __device__ __forceinline__ void init() {
-    using RT = RowTile<uint16_t, D>;
-    const int l = lane_id(), g = l >> 4;
-    const int row = perm_row(l & 15);
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-      o[s] = (uint32_t)(row * RT::kUnits * 16) + (uint32_t)(((4 * s + g) ^ RT::swz(row)) << 4);
-  }
-};
-
-// TrOffsets for results in perm_row order: lane j of group g points at row
-// 4(j / 4) + sigma(g) (columns as in TrOffsets).
-template <int D>
-struct TrOffsetsPerm {
-  uint32_t o[D / 16];
-  __device__ __forceinline__ void init() {
-    using RT = RowTile<uint16_t, D>;
-    const int l = lane_id(), j = l & 15, g = l >> 4;
-    const int r = 4 * (j >> 2) + perm_sigma(g);
-    const int u0 = (j & 3) >> 1, half = j & 1;
-    const uint32_t low = (uint32_t)(((u0 ^ RT::swz(r)) << 4) | (half << 3));
-#pragma unroll
-    for (int cb = 0; cb < D / 16; ++cb)
-      o[cb] = (uint32_t)(r * RT::kUnits * 16) + (low ^ (uint32_t)(32 * cb));
-  }
-};
 
 // Per-lane byte offsets of the row-operand (ds_read_b128) reads of a tile:
 // o[s] addresses row l16 (+ 16-row multiples as immediates), elements
