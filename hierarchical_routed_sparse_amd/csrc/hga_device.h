@@ -212,7 +212,10 @@ template <typename T, int D> struct RowTile {
   static constexpr int kUnits = D * Elem<T>::kBytes / 16;   // units per row
   static constexpr int kBytes = 64 * D * Elem<T>::kBytes;
   __device__ static __forceinline__ int swz(int row) {
-    return kUnits >= 16 ? ((row & 15) ^ ((row & 1) ? 14 : 0)) : ((row >> 1) & (kUnits - 1));
+    static_assert(kUnits == 8 || kUnits >= 16, "tile rows of 8 or at least 16 units");
+    // (8-unit rows, two per bank row: row & 6 is conflict-free for the same
+    // read patterns under the same rules)
+    return kUnits >= 16 ? ((row & 15) ^ ((row & 1) ? 14 : 0)) : (row & 6);
   }
   // byte offset of logical unit u of row `row`
   __device__ static __forceinline__ int off(int row, int u) {
