@@ -39,8 +39,8 @@ KERNEL_SOURCES = {
     "route": ["route.hip"],
     "attend_fwd": ["attend_fwd.hip"],
     "attend_bwd_dq": ["attend_bwd.hip"],
-    "attend_bwd_dkdv": ["attend_bwd.hip"],
-    "attend_bwd_dkdv_order": ["attend_bwd.hip"],
+    "attend_bwd_dkdv": ["attend_bwd_dkdv.hip", "bwd_common.h"],
+    "attend_bwd_dkdv_order": ["attend_bwd_dkdv.hip", "bwd_common.h"],
     "decode_route": ["route.hip"],
     "decode_attend": ["decode.hip"],
 }
