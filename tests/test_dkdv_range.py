@@ -59,3 +59,29 @@ def test_range_rows_equal_full_call(name):
         assert torch.equal(dV2[:, :, k0:k1], dV[:, :, k0:k1]), (c0, c1)
         assert torch.isnan(dK2[:, :, :k0]).all() and torch.isnan(dK2[:, :, k1:]).all()
         assert torch.isnan(dV2[:, :, :k0]).all() and torch.isnan(dV2[:, :, k1:]).all()
+
+
+def test_range_call_leaves_the_full_range_order_intact():
+    """The dQ call writes the whole range's dK/dV work order into the
+    workspace; a chunk sub-range call orders its own range in a second
+    buffer.  A full-range dK/dV call after a sub-range call on the same
+    workspace must still equal the full backward bit for bit."""
+    w, _ = CASES["bf16_b2_1k"]
+    print("[case] dkdv full after range", flush=True)
+    s, x, t, out = run_forward(w)
+    x.update(syn.make_inputs(w, with_grad_output=True))
+    dO = syn.to_torch(x["dO"], w.dtype, DEV)
+    dQ, dK, dV = hga.backward(s, t["Q"], t["K"], t["V"], out["O"], out["lse"], dO,
+                              out["group_idx"])
+    ws = torch.empty(hga.hga_attend_bwd_workspace(s), dtype=torch.uint8, device=DEV)
+    dQ2 = torch.empty_like(dQ)
+    hga.hga_attend_bwd_dq(s, t["Q"], t["K"], t["V"], out["O"], out["lse"], dO, out["group_idx"],
+                          dQ2, ws)
+    dK2 = torch.full_like(dK, float("nan"))
+    dV2 = torch.full_like(dV, float("nan"))
+    hga.hga_attend_bwd_dkdv_range(s, t["Q"], t["K"], t["V"], out["lse"], dO, out["group_idx"],
+                                  3, 9, dK2, dV2, ws)
+    hga.hga_attend_bwd_dkdv(s, t["Q"], t["K"], t["V"], out["lse"], dO, out["group_idx"],
+                            dK2, dV2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dK2, dK) and torch.equal(dV2, dV)
