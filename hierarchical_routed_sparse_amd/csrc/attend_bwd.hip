@@ -106,6 +106,7 @@ __device__ __forceinline__ void dq_order_block(const DqP& p, int bh, int* s_mem)
   for (int rr = tid; rr < nrows; rr += NT) {
     const int hq = hkv * r + rr / p.nblk, blk = rr % p.nblk;
     atomicAdd(&s_cnt[p.q0 / kChunk + blk], 1);   // the row's own chunk
+    if (p.top_g == 0) continue;   // no groups kept (the indices may be absent)
     const int32_t* g = p.gidx + (((long long)b * p.Hq + hq) * p.nblk + blk) * p.top_g;
     int prev = -1;
     for (int i0 = 0; i0 < p.top_g; i0 += kBatch) {

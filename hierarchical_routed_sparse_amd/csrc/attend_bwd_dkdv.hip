@@ -174,8 +174,9 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
   const int l16 = lane & 15, g4 = lane >> 4;
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
-  // work items of one (b, kv head) in the order the ordering kernel chose:
-  // chunks with the most entries first (see dkdv_order_kernel)
+  // work items of one (b, kv head) in their work order: chunks with the most
+  // entries first (written by the dQ pass for the whole range, or by
+  // dkdv_order_kernel for a sub-range)
   const int bh = w / p.nrange, c = p.order[bh * p.nrange + w % p.nrange];
   const int b = bh / p.Hkv, hkv = bh % p.Hkv;
   const int r = p.Hq / p.Hkv;
