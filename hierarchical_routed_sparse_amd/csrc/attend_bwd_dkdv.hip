@@ -270,30 +270,99 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
           sacc[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
           dpacc[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-          const char* qp = qt + qro.o[s];
+        // lse and delta of queries 16qs + 4g .. 16qs + 4g + 3 (wave-slot qs
+        // of the stats block is [lse 16 | delta 16])
+        float4 l4[4], d4[4];
+        auto read_stats = [&]() {
 #pragma unroll
           for (int qs = 0; qs < 4; ++qs) {
-            Frag<T> a;
-            frag_rows_at<T, D>(a, qp + 16 * qs * RB);
-            mma(sacc[qs], a, kf[s]);
-            frag_rows_at<T, D>(a, qp + kTileBytes + 16 * qs * RB);
-            mma(dpacc[qs], a, vf[s]);
+            l4[qs] = *reinterpret_cast<const float4*>(stat + 32 * qs + 4 * g4);
+            d4[qs] = *reinterpret_cast<const float4*>(stat + 32 * qs + 16 + 4 * g4);
           }
+        };
+        // transposed operands of column blocks cc, cc + 1: fo (dO) and fq (Q),
+        // fragment 2j + mm of block cc + j covers queries 32mm + 4g + t and
+        // 32mm + 16 + 4g + t
+        Frag<T> fo[2][4], fq[2][4];
+        auto tr_addr = [&](uint32_t (&a)[8], int cc) {
+          const uint32_t a0 = lds_addr(qt) + qto.o[cc], a1 = lds_addr(qt) + qto.o[cc + 1];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) { a[k] = a0; a[4 + k] = a1; }
+        };
+        auto read_tr_o = [&](Frag<T> (&o)[4], int cc) {
+          if constexpr (sizeof(T) == 2) {
+            uint32_t a[8];
+            tr_addr(a, cc);
+            tr_read8_sched<kTileBytes, kTileBytes + 16 * RB, kTileBytes + 32 * RB, kTileBytes + 48 * RB,
+                           kTileBytes, kTileBytes + 16 * RB, kTileBytes + 32 * RB, kTileBytes + 48 * RB>(o, a);
+          }
+        };
+        auto read_tr_q = [&](Frag<T> (&q)[4], int cc) {
+          if constexpr (sizeof(T) == 2) {
+            uint32_t a[8];
+            tr_addr(a, cc);
+            tr_read8_sched<0, 16 * RB, 32 * RB, 48 * RB, 0, 16 * RB, 32 * RB, 48 * RB>(q, a);
+          }
+        };
+
+        if constexpr (sizeof(T) == 2) {
+          // S = Q . K^T and dP = dO . V^T, software-pipelined: the 8 row
+          // operands of step s + 1 (or, after the last step, the stats) are
+          // read while the 8 products of step s run.  The scheduling fences
+          // keep the compiler from sinking the reads to their uses.
+          Frag<T> ra[2][8];
+          auto read_rows = [&](Frag<T> (&f)[8], int s) {
+            const char* qp = qt + qro.o[s];
+#pragma unroll
+            for (int qs = 0; qs < 4; ++qs) {
+              frag_rows_at<T, D>(f[2 * qs], qp + 16 * qs * RB);
+              frag_rows_at<T, D>(f[2 * qs + 1], qp + kTileBytes + 16 * qs * RB);
+            }
+          };
+          read_rows(ra[0], 0);
+#pragma unroll
+          for (int s = 0; s < D / 32; ++s) {
+            if (s + 1 < D / 32) read_rows(ra[(s + 1) & 1], s + 1);
+            else read_stats();
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int qs = 0; qs < 4; ++qs) {
+              mma(sacc[qs], ra[s & 1][2 * qs], kf[s]);
+              mma(dpacc[qs], ra[s & 1][2 * qs + 1], vf[s]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // the first column pair's transposed operands load during the softmax
+          read_tr_o(fo[0], 0);
+          read_tr_q(fq[0], 0);
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+#pragma unroll
+          for (int s = 0; s < D / 32; ++s) {
+            const char* qp = qt + qro.o[s];
+#pragma unroll
+            for (int qs = 0; qs < 4; ++qs) {
+              Frag<T> a;
+              frag_rows_at<T, D>(a, qp + 16 * qs * RB);
+              mma(sacc[qs], a, kf[s]);
+              frag_rows_at<T, D>(a, qp + kTileBytes + 16 * qs * RB);
+              mma(dpacc[qs], a, vf[s]);
+            }
+          }
+          read_stats();
         }
         // P (zero for unattended pairs) and dS; a key outside the row's kept
-        // groups gets lse = +inf, so P = exp2(-inf) = 0
+        // groups gets an exponent offset of -inf, so P = exp2(-inf) = 0 (the
+        // offset is added, not selected, so the stats are read unconditionally)
         const bool kvalid = local || ((ent >> (kin >> 3)) & 1u);
+        const float koff = kvalid ? 0.f : -INFINITY;
 #pragma unroll
         for (int qs = 0; qs < 4; ++qs) {
-          // queries 16qs + 4g + i: stats of wave-slot qs at [lse 16 | delta 16]
-          const float4 l4 = *reinterpret_cast<const float4*>(stat + 32 * qs + 4 * g4);
-          const float4 d4 = *reinterpret_cast<const float4*>(stat + 32 * qs + 16 + 4 * g4);
-          const float lq[4] = {l4.x, l4.y, l4.z, l4.w}, dq[4] = {d4.x, d4.y, d4.z, d4.w};
+          const float lq[4] = {l4[qs].x, l4[qs].y, l4[qs].z, l4[qs].w};
+          const float dq[4] = {d4[qs].x, d4[qs].y, d4[qs].z, d4[qs].w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float nl = kvalid ? -lq[i] * kLog2e : -INFINITY;
+            const float nl = fmaf(-lq[i], kLog2e, koff);
             float pr = __builtin_amdgcn_exp2f(fmaf(sacc[qs][i], c2, nl));
             if (local && kin > 16 * qs + 4 * g4 + i) pr = 0.f;
             sacc[qs][i] = pr;
@@ -305,28 +374,32 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
         frag_from_acc(pf[1], sacc[2], sacc[3]);
         frag_from_acc(dsf[0], dpacc[0], dpacc[1]);
         frag_from_acc(dsf[1], dpacc[2], dpacc[3]);
-        // dV^T += dO^T . P and dK^T += Q^T . dS; the transposed operands cover
-        // queries 32mm + 4g + t, 32mm + 16 + 4g + t of column block cb
+        // dV^T += dO^T . P and dK^T += Q^T . dS
         if constexpr (sizeof(T) == 2) {
-          uint32_t qa[D / 16];
+          // column pair i + 1's transposed reads are in flight while pair i's
+          // products run (dO reads before pair i's dV products, Q reads after
+          // its dK products: at most 16 reads outstanding); per accumulator
+          // the order is mm = 0, then 1
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int cc = 0; cc < D / 16; ++cc) qa[cc] = lds_addr(qt) + qto.o[cc];
-#pragma unroll
-          for (int cc = 0; cc < D / 16; cc += 2) {
-            const uint32_t a[8] = {qa[cc], qa[cc], qa[cc], qa[cc],
-                                   qa[cc + 1], qa[cc + 1], qa[cc + 1], qa[cc + 1]};
-            Frag<T> fo[4], fq[4];
-            tr_read8_sched<kTileBytes, kTileBytes + 16 * RB, kTileBytes + 32 * RB, kTileBytes + 48 * RB,
-                         kTileBytes, kTileBytes + 16 * RB, kTileBytes + 32 * RB, kTileBytes + 48 * RB>(fo, a);
-            tr_read8_sched<0, 16 * RB, 32 * RB, 48 * RB, 0, 16 * RB, 32 * RB, 48 * RB>(fq, a);
-            mma(dvacc[cc], fo[0], pf[0]);
-            mma(dvacc[cc], fo[1], pf[1]);
-            mma(dvacc[cc + 1], fo[2], pf[0]);
-            mma(dvacc[cc + 1], fo[3], pf[1]);
-            mma(dkacc[cc], fq[0], dsf[0]);
-            mma(dkacc[cc], fq[1], dsf[1]);
-            mma(dkacc[cc + 1], fq[2], dsf[0]);
-            mma(dkacc[cc + 1], fq[3], dsf[1]);
+          for (int i = 0; i < D / 32; ++i) {
+            const int cc = 2 * i;
+            const bool more = i + 1 < D / 32;
+            if (more) read_tr_o(fo[(i + 1) & 1], cc + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            const Frag<T>(&o)[4] = fo[i & 1];
+            const Frag<T>(&q)[4] = fq[i & 1];
+            mma(dvacc[cc], o[0], pf[0]);
+            mma(dvacc[cc + 1], o[2], pf[0]);
+            mma(dvacc[cc], o[1], pf[1]);
+            mma(dvacc[cc + 1], o[3], pf[1]);
+            mma(dkacc[cc], q[0], dsf[0]);
+            mma(dkacc[cc + 1], q[2], dsf[0]);
+            mma(dkacc[cc], q[1], dsf[1]);
+            mma(dkacc[cc + 1], q[3], dsf[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) read_tr_q(fq[(i + 1) & 1], cc + 2);
+            __builtin_amdgcn_sched_barrier(0);
           }
         } else {
           const char* ot = qt + kTileBytes;
@@ -334,11 +407,11 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
           for (int dd = 0; dd < D / 16; ++dd)
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm) {
-              Frag<T> fo, fq;
-              frag_tr<T, D>(fo, ot, 32 * mm + 4 * g4, 32 * mm + 16 + 4 * g4, 16 * dd);
-              frag_tr<T, D>(fq, qt, 32 * mm + 4 * g4, 32 * mm + 16 + 4 * g4, 16 * dd);
-              mma(dvacc[dd], fo, pf[mm]);
-              mma(dkacc[dd], fq, dsf[mm]);
+              Frag<T> o1, q1;
+              frag_tr<T, D>(o1, ot, 32 * mm + 4 * g4, 32 * mm + 16 + 4 * g4, 16 * dd);
+              frag_tr<T, D>(q1, qt, 32 * mm + 4 * g4, 32 * mm + 16 + 4 * g4, 16 * dd);
+              mma(dvacc[dd], o1, pf[mm]);
+              mma(dkacc[dd], q1, dsf[mm]);
             }
         }
       }
