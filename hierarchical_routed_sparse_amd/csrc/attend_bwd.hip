@@ -241,7 +241,16 @@ void attend_bwd_dq_kernel(const DqP p) {
   }
 
   const uint32_t smem_lds = lds_addr(smem);
-  auto issue = [&](int ti) {
+  // kept-group list entries of the rows this lane gathers for tile ti (read
+  // ahead of the issue, so the issue itself waits on no LDS read)
+  auto glist_of = [&](int ti, int (&gm)[kIssues]) {
+#pragma unroll
+    for (int j = 0; j < kIssues; ++j) {
+      const int slot = kGroupsPerTile * (ti - kLocalTiles) + (ld_row[j] >> 3);
+      gm[j] = s_glist[slot < 0 ? 0 : (slot < kMaxTopG ? slot : kMaxTopG - 1)];
+    }
+  };
+  auto issue = [&](int ti, const int (&gm)[kIssues]) {
     const uint32_t buf = smem_lds + (uint32_t)((ti % S) * kStage);
     uint32_t off[kIssues];
 #pragma unroll
@@ -252,8 +261,7 @@ void attend_bwd_dq_kernel(const DqP p) {
         tok += (uint32_t)(ti * TK);
       } else {
         const int slot = kGroupsPerTile * (ti - kLocalTiles) + (rr >> 3);
-        const int gm = s_glist[slot < kMaxTopG ? slot : kMaxTopG - 1];
-        tok = slot < nvalid ? (uint32_t)(gm * kGroup + (rr & 7)) : tok;
+        tok = slot < nvalid ? (uint32_t)(gm[j] * kGroup + (rr & 7)) : tok;
       }
       off[j] = tok * (uint32_t)(RT::kUnits * 16) + ld_col[j];
     }
@@ -271,15 +279,23 @@ void attend_bwd_dq_kernel(const DqP p) {
 
 #pragma unroll
   for (int ti = 0; ti < S - 1; ++ti)
-    if (ti < ntiles) issue(ti);
+    if (ti < ntiles) {
+      int gm[kIssues];
+      glist_of(ti, gm);
+      issue(ti, gm);
+    }
 
   for (int ti = 0; ti < ntiles; ++ti) {
+    // group-list entries of the tile issued after the barrier: their LDS
+    // reads complete in the barrier's wait
+    int gnext[kIssues];
+    glist_of(ti + S - 1, gnext);
     const int ahead = (ntiles - 1 - ti) < (S - 2) ? (ntiles - 1 - ti) : (S - 2);
     if (ahead >= 2) wait_vmcnt<2 * kLoads>();
     else if (ahead == 1) wait_vmcnt<kLoads>();
     else wait_vmcnt<0>();
     __syncthreads();
-    if (ti + S - 1 < ntiles) issue(ti + S - 1);
+    if (ti + S - 1 < ntiles) issue(ti + S - 1, gnext);
 
     const char* kt = smem + (ti % S) * kStage;
     const char* vt = kt + kTileBytes;

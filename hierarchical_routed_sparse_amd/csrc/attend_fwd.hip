@@ -135,7 +135,16 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
   // kGroupsPerTile kept groups.  A slot past the last kept group reads the own
   // chunk (any valid row works: its scores are masked, its P is exactly zero).
   const uint32_t smem_lds = lds_addr(smem);
-  auto issue = [&](int ti) {
+  // kept-group list entries of the rows this lane gathers for tile ti (read
+  // ahead of the issue, so the issue itself waits on no LDS read)
+  auto glist_of = [&](int ti, int (&gm)[kIssues]) {
+#pragma unroll
+    for (int j = 0; j < kIssues; ++j) {
+      const int slot = kGroupsPerTile * (ti - kLocalTiles) + (ld_row[j] >> 3);
+      gm[j] = s_glist[slot < 0 ? 0 : (slot < kMaxTopG ? slot : kMaxTopG - 1)];
+    }
+  };
+  auto issue = [&](int ti, const int (&gm)[kIssues]) {
     const uint32_t buf = smem_lds + (uint32_t)((ti % S) * kStage);
     uint32_t off[kIssues];
 #pragma unroll
@@ -146,8 +155,7 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
         tok += (uint32_t)(ti * TK);
       } else {
         const int slot = kGroupsPerTile * (ti - kLocalTiles) + (rr >> 3);
-        const int gm = s_glist[slot < kMaxTopG ? slot : kMaxTopG - 1];
-        tok = slot < nvalid ? (uint32_t)(gm * kGroup + (rr & 7)) : tok;
+        tok = slot < nvalid ? (uint32_t)(gm[j] * kGroup + (rr & 7)) : tok;
       }
       off[j] = tok * (uint32_t)RB + ld_col[j];
     }
@@ -168,9 +176,17 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
 
 #pragma unroll
   for (int ti = 0; ti < S - 1; ++ti)
-    if (ti < ntiles) issue(ti);
+    if (ti < ntiles) {
+      int gm[kIssues];
+      glist_of(ti, gm);
+      issue(ti, gm);
+    }
 
   for (int ti = 0; ti < ntiles; ++ti) {
+    // group-list entries of the tile issued after the barrier: their LDS
+    // reads complete in the barrier's wait
+    int gnext[kIssues];
+    glist_of(ti + S - 1, gnext);
     // tile ti has landed once at most (tiles issued after it) x kLoads remain
     const int ahead = (ntiles - 1 - ti) < (S - 2) ? (ntiles - 1 - ti) : (S - 2);
     if (ahead >= 3) wait_vmcnt<3 * kLoads>();
@@ -178,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
     else if (ahead == 1) wait_vmcnt<kLoads>();
     else wait_vmcnt<0>();
     __syncthreads();   // tile ti visible to all; everyone is done with tile ti-1
-    if (ti + S - 1 < ntiles) issue(ti + S - 1);
+    if (ti + S - 1 < ntiles) issue(ti + S - 1, gnext);
 
     const char* kt = smem + (ti % S) * kStage;
     const char* vt = kt + kTileBytes;
