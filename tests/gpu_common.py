@@ -4,6 +4,8 @@ result into the oracle except routing indices for the attention comparison
 (so that near-tie routing differences cannot leak into output comparisons)."""
 from __future__ import annotations
 
+import math
+
 import numpy as np
 import torch
 
@@ -81,3 +83,26 @@ def assert_close(got, ref, dtype, what):
     ok, maxerr, nbad = allclose_report(got, ref, atol, rtol)
     assert ok, f"{what}: {nbad} elements beyond atol={atol} rtol={rtol}; max abs err {maxerr:.3e}"
     return maxerr
+
+
+def random_shapes(n, seed, backward=True):
+    """n valid problems drawn from a seeded generator: bf16 and fp32, D 64 and
+    128, 1 to 8 query heads per kv head, batch 1 or 2, 1 to 6 query blocks,
+    kv histories of 0 to 12 extra chunks, top-k from 0 to 20 and top-g from 0
+    to 8 groups past what the kept chunks hold (the rest is padding)."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for i in range(n):
+        dtype = "bf16" if i % 2 == 0 else "fp32"
+        D = int(rng.choice([64, 128]))
+        hkv = int(rng.integers(1, 3))
+        r = int(rng.choice([1, 2, 4, 8]))
+        q_len = 64 * int(rng.integers(1, 7))
+        kv_len = q_len + 64 * int(rng.integers(0, 13))
+        top_k = int(rng.integers(0, 21))
+        top_g = int(rng.integers(0, 8 * top_k + 9))
+        scale = 1 / math.sqrt(D) if dtype == "bf16" else 0.3
+        name = f"rand{i}_{dtype}_d{D}_h{hkv * r}x{hkv}_q{q_len}_kv{kv_len}_k{top_k}_g{top_g}"
+        out[name] = syn.Workload(name, int(rng.integers(1, 3)), hkv * r, hkv, D, q_len, kv_len,
+                                 top_k, top_g, dtype, seed + i, scale, backward=backward)
+    return out

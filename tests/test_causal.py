@@ -15,6 +15,7 @@ import pytest
 
 import hierarchical_routed_sparse_amd as hga
 from hierarchical_routed_sparse_amd import synthetic as syn
+from gpu_common import random_shapes
 
 CASES = {
     "bf16_seg_b2": syn.Workload("c1", 2, 8, 2, 128, 256, 1024, 4, 20, "bf16", 61,
@@ -26,6 +27,9 @@ CASES = {
     "bf16_r8_k0": syn.Workload("c4", 1, 8, 1, 128, 128, 384, 0, 8, "bf16", 64,
                                1 / math.sqrt(128), backward=True),
 }
+
+
+RANDOM = random_shapes(8, seed=211)
 
 
 def _run(w, x, causal=True):
@@ -42,10 +46,20 @@ def _run(w, x, causal=True):
 @pytest.mark.gpu
 @pytest.mark.parametrize("name", list(CASES))
 def test_causal_small_case_full_parity(oracle, name):
+    _causal_full_parity(oracle, CASES[name])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", list(RANDOM))
+def test_causal_random_shapes_full_parity(oracle, name):
+    """The same comparison on seeded random valid shapes."""
+    _causal_full_parity(oracle, RANDOM[name])
+
+
+def _causal_full_parity(oracle, w):
     import torch
     from gpu_common import DEV, assert_close, check_routing, f64
-    w = CASES[name]
-    print(f"[case] causal {name}", flush=True)
+    print(f"[case] causal {w.name}", flush=True)
     x = syn.make_inputs(w, with_qprev=True)
     s, t, out = _run(w, x)
     xf = {k: syn.to_f64(v, w.dtype) for k, v in x.items()}

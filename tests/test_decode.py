@@ -41,6 +41,30 @@ CASES = {
 }
 
 
+def _random_cases(n, seed=131):
+    """n valid decode problems from a seeded generator: bf16 and fp32, D 64 and
+    128, 1 to 8 query heads per kv head, batch 1 to 3, cache lengths of 1 to
+    3000 tokens (any length, so any position within its chunk), top-k 0 to 24
+    and top-g up to 8 groups past what the kept chunks hold."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for i in range(n):
+        dtype = "bf16" if i % 2 == 0 else "fp32"
+        D = int(rng.choice([64, 128]))
+        hkv = int(rng.integers(1, 3))
+        r = int(rng.choice([1, 2, 4, 8]))
+        L = int(rng.integers(1, 3001))
+        k = int(rng.integers(0, 25))
+        g = int(rng.integers(0, 8 * k + 9))
+        name = f"rand{i}_{dtype}_d{D}_h{hkv * r}x{hkv}_L{L}_k{k}_g{g}"
+        out[name] = _workload(name, int(rng.integers(1, 4)), hkv * r, hkv, D, L, k, g, dtype,
+                              500 + i)
+    return out
+
+
+RANDOM = _random_cases(10)
+
+
 def _cap(L):
     return max(64, -(-L // 64) * 64)
 
@@ -167,6 +191,17 @@ def _check(oracle, w, x, out, batches=None):
 @pytest.mark.parametrize("name", list(CASES))
 def test_decode_small_case_parity(oracle, name):
     w = CASES[name]
+    print(f"[case] decode {name}", flush=True)
+    x = syn.make_inputs(w)
+    out = _run(w, x)
+    _check(oracle, w, x, out)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", list(RANDOM))
+def test_decode_random_shapes_parity(oracle, name):
+    """The same comparison on seeded random valid decode problems."""
+    w = RANDOM[name]
     print(f"[case] decode {name}", flush=True)
     x = syn.make_inputs(w)
     out = _run(w, x)

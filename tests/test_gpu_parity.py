@@ -16,7 +16,8 @@ import torch
 
 import hierarchical_routed_sparse_amd as hga
 from hierarchical_routed_sparse_amd import synthetic as syn
-from gpu_common import DEV, assert_close, check_routing, f64, run_forward, shape_of, upload
+from gpu_common import (DEV, assert_close, check_routing, f64, random_shapes, run_forward,
+                        shape_of, upload)
 from hga_testlib import (causal_mask, hand_example_inputs, hand_example_output_e1,
                          load_golden, sdpa_f64)
 
@@ -48,30 +49,7 @@ def _oracle_inputs(w, x):
     return {k: syn.to_f64(v, w.dtype) for k, v in x.items()}
 
 
-def _random_shapes(n, seed=97):
-    """n valid problems drawn from a seeded generator: bf16 and fp32, D 64 and
-    128, 1 to 8 query heads per kv head, batch 1 or 2, 1 to 6 query blocks,
-    kv histories of 0 to 12 extra chunks, top-k from 0 to 20 and top-g from 0
-    to 8 groups past what the kept chunks hold (the rest is padding)."""
-    rng = np.random.default_rng(seed)
-    out = {}
-    for i in range(n):
-        dtype = "bf16" if i % 2 == 0 else "fp32"
-        D = int(rng.choice([64, 128]))
-        hkv = int(rng.integers(1, 3))
-        r = int(rng.choice([1, 2, 4, 8]))
-        q_len = 64 * int(rng.integers(1, 7))
-        kv_len = q_len + 64 * int(rng.integers(0, 13))
-        top_k = int(rng.integers(0, 21))
-        top_g = int(rng.integers(0, 8 * top_k + 9))
-        scale = 1 / math.sqrt(D) if dtype == "bf16" else 0.3
-        name = f"rand{i}_{dtype}_d{D}_h{hkv * r}x{hkv}_q{q_len}_kv{kv_len}_k{top_k}_g{top_g}"
-        out[name] = syn.Workload(name, int(rng.integers(1, 3)), hkv * r, hkv, D, q_len, kv_len,
-                                 top_k, top_g, dtype, 300 + i, scale, backward=True)
-    return out
-
-
-RANDOM = _random_shapes(12)
+RANDOM = random_shapes(12, seed=97)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
