@@ -377,9 +377,8 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
         // dV^T += dO^T . P and dK^T += Q^T . dS
         if constexpr (sizeof(T) == 2) {
           // column pair i + 1's transposed reads are in flight while pair i's
-          // products run (dO reads before pair i's dV products, Q reads after
-          // its dK products: at most 16 reads outstanding); per accumulator
-          // the order is mm = 0, then 1
+          // products run (its dO reads go out before pair i's products, its Q
+          // reads after them); per accumulator the order is mm = 0, then 1
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int i = 0; i < D / 32; ++i) {
