@@ -43,6 +43,7 @@ KERNEL_SOURCES = {
     "attend_bwd_dkdv_order": ["attend_bwd_dkdv.hip", "bwd_common.h"],
     "decode_route": ["route.hip"],
     "decode_attend": ["decode.hip"],
+    "gather": ["attend_fwd.hip"],
 }
 
 
@@ -60,7 +61,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="segment_2k_over_16k")
+    ap.add_argument("--workload", default="segment_2k_over_16k",
+                    help="segment_2k_over_16k (the headline), causal_16k, fwd_bwd_b2_4k, "
+                         "qwen3_8b_2k, segment_2k_over_64k_ties, tiny_fp32_1k")
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time the forward step only (summaries, routing, attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -80,9 +85,15 @@ def parse():
 
 
 def algorithmic_work(w, pairs: int) -> dict:
-    """Per-launch algorithmic bytes or flops of each phase (one launch per step)."""
+    """Per-launch algorithmic bytes or flops of each phase (one launch per
+    step).  Flops count the products the method needs, 2*D per attended pair
+    and product: the forward's two (Q.K^T, P.V), the backward's five
+    (Q.K^T and dO.V^T for P and dP, then dS.K for dQ, P^T.dO for dV and
+    dS^T.Q for dK), of which the dQ call needs the first three and the dK/dV
+    call the last two.  The recomputation of Q.K^T and dO.V^T in the dK/dV
+    kernel is not counted here (see executed_work)."""
     B, Hq, Hkv, D, Sq, Skv = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.q_len, w.kv_len
-    esz = 2
+    esz = 2 if w.dtype == "bf16" else 4
     means = B * Hkv * (Skv // 64 + Skv // 8) * D * 4
     idx = B * Hq * (Sq // 64) * (w.top_k + w.top_g) * 4
     return {
@@ -94,8 +105,37 @@ def algorithmic_work(w, pairs: int) -> dict:
         "attend_fwd": ("mfma", 4 * D * pairs),
         # Q.K^T, dO.V^T, dS.K
         "attend_bwd_dq": ("mfma", 6 * D * pairs),
-        # Q.K^T, dO.V^T, P^T.dO, dS^T.Q
-        "attend_bwd_dkdv": ("mfma", 8 * D * pairs),
+        # P^T.dO, dS^T.Q
+        "attend_bwd_dkdv": ("mfma", 4 * D * pairs),
+    }
+
+
+def executed_work(group_idx, D: int) -> dict:
+    """MFMA flops the attention kernels issue per launch, counted from their
+    tiling and the routing: the forward and dQ kernels walk 32-key tiles (the
+    own chunk as two tiles, then the kept groups four per tile) for the 64
+    queries of a routing row, 2*D flops per (query, key) slot and product (2
+    products forward, 3 for dQ); the dK/dV kernel takes, for every (routing
+    row, chunk) it attends, the 16-key slices (group pairs) with a kept group
+    (all four for the own chunk) against the 64 queries, with 4 products
+    (Q.K^T and dO.V^T recomputed, then P^T.dO and dS^T.Q).  Masked slots
+    count: this is what the matrix cores execute, not the method's work."""
+    import numpy as np
+    gi = group_idx.reshape(-1, group_idx.shape[-1])
+    kept = (gi >= 0).sum(axis=1)
+    tiles = 2 + (kept + 3) // 4
+    slots = int(tiles.sum()) * 32 * 64
+    g = np.where(gi >= 0, gi, -1)
+    # distinct (chunk, group pair) per row: (g >> 1) identifies the pair
+    pairs = 0
+    for row in g:
+        v = row[row >= 0]
+        pairs += len(np.unique(v >> 1))
+    slices = pairs + 4 * gi.shape[0]
+    return {
+        "attend_fwd": 4 * D * slots,
+        "attend_bwd_dq": 6 * D * slots,
+        "attend_bwd_dkdv": 8 * D * slices * 16 * 64,
     }
 
 
@@ -115,7 +155,7 @@ KERNEL_NAMES = {
     "summaries": "summaries_kernel", "route": "route_kernel", "attend_fwd": "attend_fwd_kernel",
     "attend_bwd_dq": "attend_bwd_dq_kernel", "attend_bwd_dkdv": "attend_bwd_dkdv_kernel",
     "attend_bwd_dkdv_order": "dkdv_order_kernel", "decode_route": "route_kernel",
-    "decode_attend": "decode_kernel",
+    "decode_attend": "decode_kernel", "gather": "attend_fwd_kernel (gather-only build)",
 }
 
 
@@ -137,43 +177,142 @@ def load_traffic(phase: str):
     return total
 
 
-def cpu_baseline(w, x, budget_s: float = 12.0, causal: bool = False):
-    """The CPU oracle, single thread, on whole kv heads of the same inputs (each
-    with its query heads: summaries, routing, attention forward and backward in
-    fp64), taken one after another until `budget_s` seconds of work are done;
-    the rate is scaled from that sample to the whole layer."""
+def cpu_host():
+    """The host's CPU model and the threads this process may use (capped at
+    16, the CPU share of one GPU on the measurement boxes)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return model, n, min(n, 16)
+
+
+def cpu_baseline(w, x, budget_s: float = 12.0, causal: bool = False, fwd_only: bool = False,
+                 parallel_s: float = 4.0, span: int = 8):
+    """The CPU oracle on the same inputs, timed two ways.
+
+    Work unit: the routing rows of one (b, kv head) over `span` consecutive
+    64-query blocks (all of the kv head's query heads), run as the oracle's
+    segment at the end of its own prefix of the history: routing over the
+    prefix's summaries, attention forward and, unless `fwd_only`, the
+    backward.  That is exactly those rows' share of the layer's work (the
+    unit's dK/dV are partial sums of the layer's).  Units are taken in a
+    seeded random order.  The summaries of every kv head are timed once in
+    full.  Single thread: units one after another until `budget_s` seconds;
+    all cores: the same units on a pool of host threads (the oracle is C,
+    called through ctypes, which releases the interpreter lock) until
+    `parallel_s` seconds of wall time.  Each rate is scaled from its sample
+    of units to the whole layer."""
+    import concurrent.futures as cf
+    import threading
+    import numpy as np
     import oracle
     from hierarchical_routed_sparse_amd import synthetic as syn
-    r = w.n_q_heads // w.n_kv_heads
     oracle.build(force=False)
-    units = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
-    done, dt = 0, 0.0
-    for b, h in units:
-        xs = {"Q": x["Q"][b:b + 1, h * r:(h + 1) * r], "K": x["K"][b:b + 1, h:h + 1],
-              "V": x["V"][b:b + 1, h:h + 1], "dO": x["dO"][b:b + 1, h * r:(h + 1) * r]}
+    B, Hq, Hkv = w.batch, w.n_q_heads, w.n_kv_heads
+    r, nblk, q0 = Hq // Hkv, w.q_len // 64, w.kv_len - w.q_len
+    span = min(span, nblk)
+    Kf = syn.to_f64(x["K"], w.dtype)
+    Vf = syn.to_f64(x["V"], w.dtype)
+    t0 = time.perf_counter()
+    cm, gm = oracle.summaries(Kf)
+    t_summ = time.perf_counter() - t0
+    units = [(b, hk, j) for b in range(B) for hk in range(Hkv) for j in range(0, nblk, span)]
+    order = np.random.default_rng(0).permutation(len(units))
+
+    def prep(i):
+        b, hk, j = units[i]
+        hs = slice(hk * r, (hk + 1) * r)
+        n = min(span, nblk - j)
+        end = q0 + 64 * (j + n)    # the unit's prefix: keys up to its last block's chunk
+        qs = slice(64 * j, 64 * (j + n))
+        u = {"Q": syn.to_f64(x["Q"][b:b + 1, hs, qs], w.dtype)}
+        if not fwd_only:
+            u["dO"] = syn.to_f64(x["dO"][b:b + 1, hs, qs], w.dtype)
         if causal:
-            xs["Qprev"] = x["Qprev"][b:b + 1, h * r:(h + 1) * r]
-        xf = {k: syn.to_f64(v, w.dtype) for k, v in xs.items()}
+            u["Qprev"] = syn.to_f64(x["Q"][b:b + 1, hs, 64 * (j - 1):64 * j], w.dtype) \
+                if j > 0 else syn.to_f64(x["Qprev"][b:b + 1, hs], w.dtype)
+        return u, Kf[b:b + 1, hk:hk + 1, :end], Vf[b:b + 1, hk:hk + 1, :end], \
+            cm[b:b + 1, hk:hk + 1, :end // 64], gm[b:b + 1, hk:hk + 1, :end // 8], end
+
+    def work(u, K, V, c, g, end):
+        _, gi = oracle.route(u["Q"], c, g, end, w.top_k, w.top_g, causal=causal,
+                             Qprev=u.get("Qprev"))
+        oracle.attend_fwd(u["Q"], K, V, gi)
+        if not fwd_only:
+            oracle.attend_bwd(u["Q"], K, V, gi, u["dO"])
+
+    done, dt = 0, 0.0
+    for i in order:
+        args = prep(i)
         t0 = time.perf_counter()
-        cm, gm = oracle.summaries(xf["K"])
-        _, gi = oracle.route(xf["Q"], cm, gm, w.kv_len, w.top_k, w.top_g, causal=causal,
-                             Qprev=xf.get("Qprev"))
-        oracle.attend_fwd(xf["Q"], xf["K"], xf["V"], gi)
-        oracle.attend_bwd(xf["Q"], xf["K"], xf["V"], gi, xf["dO"])
+        work(*args)
         dt += time.perf_counter() - t0
         done += 1
         if dt >= budget_s:
             break
-    frac = len(units) / done
-    return {
-        "value": w.q_len * w.batch / (dt * frac),
+    t_layer = t_summ + dt * len(units) / done
+    model, avail, threads = cpu_host()
+    what = "routing, attention forward" + ("" if fwd_only else " and backward")
+    res = {
+        "value": w.batch * w.q_len / t_layer,
         "unit": "query tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"{done} of the {len(units)} kv heads (each with its {r} query heads) of the "
-                   f"same inputs: summaries, routing, attention forward and backward in fp64, "
-                   f"{dt:.1f} s single-threaded, rate scaled x{frac:g} to the whole layer"),
+        "sample": (f"{done} of the {len(units)} units of {span} query blocks x {r} query heads "
+                   f"(seeded random order), each the oracle's segment over its own history "
+                   f"prefix ({what}, fp64), {dt:.1f} s single-threaded, scaled "
+                   f"x{len(units) / done:.2f} to the layer, plus the summaries of the whole "
+                   f"layer ({t_summ:.2f} s)"),
+        "cpu_model": model,
+        "host_threads_available": avail,
     }
+    # all cores: a pool of threads pulling prepared units until the wall-time
+    # budget (the units' inputs are sliced before the timed region)
+    need = min(len(units), int(1.5 * threads * parallel_s * done / dt) + threads)
+    ready = [prep(i) for i in order[:need]]
+    nxt = iter(ready)
+    lock = threading.Lock()
+    counts = []
+    deadline = time.perf_counter() + parallel_s
+
+    def worker():
+        n = 0
+        while time.perf_counter() < deadline:
+            with lock:
+                a = next(nxt, None)
+            if a is None:
+                break
+            work(*a)
+            n += 1
+        counts.append(n)
+
+    t0 = time.perf_counter()
+    deadline = t0 + parallel_s
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        for f in [ex.submit(worker) for _ in range(threads)]:
+            f.result()
+    wall = time.perf_counter() - t0
+    pdone = sum(counts)
+    t_par = t_summ / threads + wall * len(units) / max(pdone, 1)
+    res["all_cores"] = {
+        "value": w.batch * w.q_len / t_par,
+        "unit": "query tokens/s",
+        "cores": threads,
+        "sample": (f"{pdone} units (the same unit work) on {threads} threads in {wall:.1f} s "
+                   f"wall, scaled x{len(units) / max(pdone, 1):.2f} to the layer; summaries "
+                   f"counted as split over the threads"),
+    }
+    return res
 
 
 def segments_main(args):
@@ -547,12 +686,14 @@ def main():
         decode_main(args)
         return
 
+    import numpy as np
     import torch
     import hierarchical_routed_sparse_amd as hga
     from hierarchical_routed_sparse_amd import synthetic as syn
 
     w = syn.WORKLOADS[args.workload]
-    x = syn.make_inputs(w, with_grad_output=True, with_qprev=args.causal)
+    fwd_only = args.fwd_only
+    x = syn.make_inputs(w, with_grad_output=not fwd_only, with_qprev=args.causal)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     t = {k: syn.to_torch(v, w.dtype, dev) for k, v in x.items()}
@@ -567,21 +708,23 @@ def main():
     gi = torch.empty(sz["gi"], dtype=i32, device=dev)
     O = torch.empty(sz["q"], dtype=edt, device=dev)
     lse = torch.empty(sz["lse"], dtype=f32, device=dev)
-    dQ = torch.empty(sz["q"], dtype=edt, device=dev)
-    dK = torch.empty(sz["kv"], dtype=edt, device=dev)
-    dV = torch.empty(sz["kv"], dtype=edt, device=dev)
-    ws = torch.empty(hga.hga_attend_bwd_workspace(s), dtype=torch.uint8, device=dev)
-    phases = ["summaries", "route", "attend_fwd", "attend_bwd_dq", "attend_bwd_dkdv"]
+    phases = ["summaries", "route", "attend_fwd"]
     calls = {
         "summaries": lambda: hga.hga_build_summaries(s, t["K"], cm, gm),
         "route": (lambda: hga.hga_route_causal(s, t["Q"], t["Qprev"], cm, gm, ci, gi))
         if args.causal else (lambda: hga.hga_route(s, t["Q"], cm, gm, ci, gi)),
         "attend_fwd": lambda: hga.hga_attend_fwd(s, t["Q"], t["K"], t["V"], gi, O, lse),
-        "attend_bwd_dq": lambda: hga.hga_attend_bwd_dq(s, t["Q"], t["K"], t["V"], O, lse,
-                                                       t["dO"], gi, dQ, ws),
-        "attend_bwd_dkdv": lambda: hga.hga_attend_bwd_dkdv(s, t["Q"], t["K"], t["V"], lse,
-                                                           t["dO"], gi, dK, dV, ws),
     }
+    if not fwd_only:
+        dQ = torch.empty(sz["q"], dtype=edt, device=dev)
+        dK = torch.empty(sz["kv"], dtype=edt, device=dev)
+        dV = torch.empty(sz["kv"], dtype=edt, device=dev)
+        ws = torch.empty(hga.hga_attend_bwd_workspace(s), dtype=torch.uint8, device=dev)
+        phases += ["attend_bwd_dq", "attend_bwd_dkdv"]
+        calls["attend_bwd_dq"] = lambda: hga.hga_attend_bwd_dq(
+            s, t["Q"], t["K"], t["V"], O, lse, t["dO"], gi, dQ, ws)
+        calls["attend_bwd_dkdv"] = lambda: hga.hga_attend_bwd_dkdv(
+            s, t["Q"], t["K"], t["V"], lse, t["dO"], gi, dK, dV, ws)
 
     def step(ev=None):
         # every call launches on the current stream (the capture stream inside
@@ -599,7 +742,8 @@ def main():
         calibration_copy(dev)
 
     # eager pass: per-phase HIP events (each phase includes its launch gap)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -612,6 +756,7 @@ def main():
     ms_step = timed_replays(graph_of(step), args.steps, args.warmup)
     pairs = attended_pairs(gi)
     work = algorithmic_work(w, pairs)
+    executed = executed_work(gi.cpu().numpy(), w.head_dim)
     phase_rep = {}
     for p in phases:
         kind, amount = work[p]
@@ -619,15 +764,22 @@ def main():
         if kind == "hbm":
             ach = amount / sec / 1e9
             phase_rep[p] = {"us": round(phase_ms[p] * 1e3, 2), "bound": "hbm",
+                            "algorithmic_bytes": amount,
                             "achieved_GBs": round(ach, 1), "frac": round(ach / PEAK_HBM_GBS, 4)}
         else:
             ach = amount / sec / 1e12
             phase_rep[p] = {"us": round(phase_ms[p] * 1e3, 2), "bound": "mfma",
+                            "algorithmic_flop": amount,
                             "achieved_TFLOPs": round(ach, 1),
-                            "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-    dom = max(phases, key=lambda p: phase_ms[p])
+                            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                            "executed_flop": executed[p],
+                            "executed_TFLOPs": round(executed[p] / sec / 1e12, 1)}
+    # kernel-only durations of every phase (back-to-back launches in a graph)
+    for p in phases:
+        phase_rep[p]["kernel_us"] = round(kernel_us(calls[p]), 2)
+    dom = max(phases, key=lambda p: phase_rep[p]["kernel_us"])
     kind, amount = work[dom]
-    dom_us = kernel_us(calls[dom])
+    dom_us = phase_rep[dom]["kernel_us"]
     sec = dom_us * 1e-6
     if kind == "hbm":
         roof = {"bound": "hbm", "achieved": amount / sec / 1e9, "peak": PEAK_HBM_GBS,
@@ -639,15 +791,57 @@ def main():
     roof["traffic"] = load_traffic(dom)
     roof["kernel"] = dom
     roof["launches"] = " + ".join(KERNEL_NAMES[k] for k in PHASE_KERNELS.get(dom, [dom]))
-    roof["kernel_us"] = round(dom_us, 2)
+    roof["kernel_us"] = dom_us
     roof["algorithmic_per_launch"] = amount
+    if kind == "mfma":
+        roof["executed_per_launch"] = executed[dom]
+        roof["executed_TFLOPs"] = executed[dom] / sec / 1e12
+    # routing and gather phases against HBM peak: summaries + route on their
+    # kernel times; the gather of the forward from its gather-only build
+    rb = work["summaries"][1] + work["route"][1]
+    rt = phase_rep["summaries"]["kernel_us"] + phase_rep["route"]["kernel_us"]
+    phase_rep["routing_total"] = {"kernel_us": round(rt, 2), "algorithmic_bytes": rb,
+                                  "achieved_GBs": round(rb / (rt * 1e-6) / 1e9, 1),
+                                  "frac": round(rb / (rt * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    if os.path.exists(hga.GATHER_LIB_PATH) and not args.causal:
+        Og = torch.empty_like(O)
+        lg = torch.empty_like(lse)
+        gus = kernel_us(lambda: hga.hga_attend_fwd(s, t["Q"], t["K"], t["V"], gi, Og, lg,
+                                                    library=hga.GATHER_LIB_PATH))
+        kept = int((gi >= 0).sum().item())
+        nrows = gi.shape[0] * gi.shape[1] * gi.shape[2]
+        esz = 2 if w.dtype == "bf16" else 4
+        logical = (kept * 8 + nrows * 64) * w.head_dim * esz * 2
+        unique = 0
+        gnp = gi.cpu().numpy()
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                r = w.n_q_heads // w.n_kv_heads
+                sel = gnp[b, h * r:(h + 1) * r]
+                own = (w.kv_len - w.q_len) // 8 + np.arange(8 * (w.q_len // 64))
+                unique += len(np.union1d(np.unique(sel[sel >= 0]), own)) * 8
+        unique *= w.head_dim * esz * 2
+        ach = logical / (gus * 1e-6) / 1e9
+        phase_rep["gather"] = {
+            "kernel_us": round(gus, 2), "bound": "hbm", "logical_bytes": logical,
+            "unique_bytes": unique, "achieved_GBs": round(ach, 1),
+            "frac_logical": round(ach / PEAK_HBM_GBS, 4),
+            "unique_GBs": round(unique / (gus * 1e-6) / 1e9, 1),
+            "traffic": load_traffic("gather"),
+            "note": "the forward kernel built without its products (same routing-row load, "
+                    "tile walk, direct loads, waits and barriers); logical bytes count every "
+                    "gathered K and V row each time it is gathered, most served from the "
+                    "GPU's caches, so the logical rate may exceed the HBM peak"}
 
     base = None
     if not args.no_cpu_baseline:
-        base = cpu_baseline(w, x, causal=args.causal)
+        base = cpu_baseline(w, x, causal=args.causal, fwd_only=fwd_only)
 
+    what = "fwd" if fwd_only else "fwd+bwd"
+    metric = METRIC if (w.name == "segment_2k_over_16k" and not fwd_only) else \
+        f"HGA {what} query tokens/sec, {w.name}, 1 MI355X; % HBM / % MFMA peak"
     out = {
-        "metric": METRIC + (" (strictly causal routing)" if args.causal else ""),
+        "metric": metric + (" (strictly causal routing)" if args.causal else ""),
         "value": w.batch * w.q_len / (ms_step * 1e-3),
         "unit": "query tokens/s",
         "n_gpus": 1,
@@ -661,7 +855,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded clustered keys, N(0,1)/sqrt(128) queries and values)",
         "config": {
-            "workload": f"{w.name} fwd+bwd" + (", strictly causal routing" if args.causal else ""),
+            "workload": f"{w.name} {what}" + (", strictly causal routing" if args.causal else ""),
             "batch": w.batch, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "q_len": w.q_len, "kv_len": w.kv_len,
             "chunk": 64, "group": 8, "top_k": w.top_k, "top_g": w.top_g,

@@ -65,22 +65,26 @@ def make_shape(batch, n_q_heads, n_kv_heads, head_dim, q_len, kv_len, top_k, top
                     float(softmax_scale), int(dt), int(kv_capacity))
 
 
-_lib = None
+_libs = {}
 _vp = ctypes.c_void_p
 _SP = ctypes.POINTER(HgaShape)
+# the gather-only measurement build of the library (the forward kernel with its
+# products left out); only the benchmark's gather phase calls it
+GATHER_LIB_PATH = os.path.join(HERE, "libhga_gather.so")
 
 
 def lib_path() -> str:
     return LIB_PATH
 
 
-def _load():
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise HGAError(f"{LIB_PATH} is not built; run python -m hierarchical_routed_sparse_amd.build_lib")
-    lib = ctypes.CDLL(LIB_PATH)
+def _load(path: str = None):
+    path = path or LIB_PATH
+    lib = _libs.get(path)
+    if lib is not None:
+        return lib
+    if not os.path.exists(path):
+        raise HGAError(f"{path} is not built; run python -m hierarchical_routed_sparse_amd.build_lib")
+    lib = ctypes.CDLL(path)
     i32, sz = ctypes.c_int32, ctypes.c_size_t
     lib.hga_abi_version.restype = ctypes.c_int
     lib.hga_status_str.restype = ctypes.c_char_p
@@ -105,7 +109,7 @@ def _load():
                  "hga_attend_bwd_workspace", "hga_attend_bwd", "hga_attend_bwd_dq",
                  "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range"):
         getattr(lib, name).restype = ctypes.c_int
-    _lib = lib
+    _libs[path] = lib
     return lib
 
 
@@ -264,10 +268,11 @@ def hga_route_causal(shape, Q, Q_prev, chunk_mean, group_mean, chunk_idx, group_
         _stream(stream)), "hga_route_causal")
 
 
-def hga_attend_fwd(shape, Q, K, V, group_idx, O, lse=None, stream=None):
+def hga_attend_fwd(shape, Q, K, V, group_idx, O, lse=None, stream=None, library=None):
+    """``library``: GATHER_LIB_PATH selects the gather-only measurement build."""
     import torch
     sz, dt = _sizes(shape), _elt_dtype(shape)
-    _check(_load().hga_attend_fwd(
+    _check(_load(library).hga_attend_fwd(
         ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"], host_ok=True),
         _ptr(V, "V", dt, sz["kv"], host_ok=True),
         _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),

@@ -40,32 +40,6 @@ namespace {
 
 constexpr int kMaxTopG = 512;
 
-// Compacts the routing row (groups in [0, 8*cb), order kept) into s_glist and
-// returns how many were kept.  Every thread of the workgroup must call it.
-__device__ __forceinline__ int load_routing_row(const int32_t* grow, int top_g, int cb,
-                                                int* s_glist, int* s_wsum) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int nvalid = 0;
-  for (int i0 = 0; i0 < top_g; i0 += kThreads) {
-    const int i = i0 + tid;
-    const int gm = i < top_g ? grow[i] : -1;
-    const bool ok = gm >= 0 && gm < cb * 8;
-    const uint64_t bal = __ballot(ok);
-    if (lane == 0) s_wsum[wv] = __popcll(bal);
-    __syncthreads();
-    int off = 0, tot = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      off += k < wv ? s_wsum[k] : 0;
-      tot += s_wsum[k];
-    }
-    if (ok) s_glist[nvalid + off + mbcnt(bal)] = gm;
-    nvalid += tot;
-    __syncthreads();
-  }
-  return nvalid;
-}
-
 // ============================================================== dQ
 
 struct DqP {
@@ -108,17 +82,23 @@ __device__ __forceinline__ void dq_order_block(const DqP& p, int bh, int* s_mem)
     atomicAdd(&s_cnt[p.q0 / kChunk + blk], 1);   // the row's own chunk
     if (p.top_g == 0) continue;   // no groups kept (the indices may be absent)
     const int32_t* g = p.gidx + (((long long)b * p.Hq + hq) * p.nblk + blk) * p.top_g;
-    int prev = -1;
-    for (int i0 = 0; i0 < p.top_g; i0 += kBatch) {
+    // the row's kept groups as the attention kernels take them (see
+    // load_routing_prefix): the ascending prefix of groups before the own
+    // chunk; a chunk's groups are then consecutive entries
+    const int limit = 8 * (p.q0 / kChunk + blk);
+    int prev_g = -1, prev_c = -1;
+    bool open = true;
+    for (int i0 = 0; i0 < p.top_g && open; i0 += kBatch) {
       int v[kBatch];
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) v[k] = i0 + k < p.top_g ? g[i0 + k] : -1;
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
-        // kept groups are ascending: a chunk's groups are consecutive entries
-        const int c = v[k] >= 0 ? v[k] >> 3 : -1;
-        if (c >= 0 && c != prev) atomicAdd(&s_cnt[c], 1);
-        prev = c >= 0 ? c : prev;
+        open = open && v[k] >= 0 && v[k] < limit && v[k] > prev_g;
+        const int c = v[k] >> 3;
+        if (open && c != prev_c) atomicAdd(&s_cnt[c], 1);
+        prev_g = open ? v[k] : prev_g;
+        prev_c = open ? c : prev_c;
       }
     }
   }
@@ -197,7 +177,8 @@ void attend_bwd_dq_kernel(const DqP p) {
   const int cb = p.q0 / kChunk + blk;
   const long long row = ((long long)b * p.Hq + hq) * p.nblk + blk;
 
-  const int nvalid = load_routing_row(p.gidx + row * p.top_g, p.top_g, cb, s_glist, s_wsum);
+  const int nvalid = load_routing_prefix<kThreads>(p.gidx + row * p.top_g, p.top_g, cb * 8,
+                                                   s_glist, s_wsum);
   const int ntiles = kLocalTiles + (nvalid + kGroupsPerTile - 1) / kGroupsPerTile;
 
   const T* Kbh = reinterpret_cast<const T*>(p.K) + (long long)bh * p.Scap * D;

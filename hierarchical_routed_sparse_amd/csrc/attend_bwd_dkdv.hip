@@ -178,6 +178,10 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
   // entries first (written by the dQ pass for the whole range, or by
   // dkdv_order_kernel for a sub-range)
   const int bh = w / p.nrange, c = p.order[bh * p.nrange + w % p.nrange];
+  // the order comes from the workspace: a chunk outside the range (a
+  // workspace not written by the matching dQ or ordering pass) is skipped, so
+  // no store ever leaves the range's rows of dK and dV
+  if (c < p.chunk0 || c >= p.chunk0 + p.nrange) return;
   const int b = bh / p.Hkv, hkv = bh % p.Hkv;
   const int r = p.Hq / p.Hkv;
   const int nrows = r * p.nblk;          // (query head in group, block), head-major

@@ -29,6 +29,13 @@
 #ifndef HGA_FWD_STAGES
 #define HGA_FWD_STAGES 2    // tiles resident in LDS (STAGES - 1 in flight)
 #endif
+// HGA_GATHER_ONLY=1 builds a measurement variant of this kernel (its own
+// library, never the product): the same routing-row load, tile walk, direct
+// loads, waits and barriers, with the products and the softmax left out, so
+// that its time is the gather's alone.  It writes O = 0 and lse = 0.
+#ifndef HGA_GATHER_ONLY
+#define HGA_GATHER_ONLY 0
+#endif
 
 namespace hga {
 namespace {
@@ -84,25 +91,9 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
   const int cb = p.q0 / kChunk + blk;
   const long long row = ((long long)b * p.Hq + hq) * p.nblk + blk;
 
-  // routing row -> LDS, keeping only groups in [0, 8*cb), compacted in order
-  int nvalid = 0;
-  for (int i0 = 0; i0 < p.top_g; i0 += kThreads) {
-    const int i = i0 + tid;
-    const int gm = i < p.top_g ? p.gidx[row * p.top_g + i] : -1;
-    const bool ok = gm >= 0 && gm < cb * 8;
-    const uint64_t bal = __ballot(ok);
-    if (lane == 0) s_wsum[wv] = __popcll(bal);
-    __syncthreads();
-    int off = 0, tot = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      off += k < wv ? s_wsum[k] : 0;
-      tot += s_wsum[k];
-    }
-    if (ok) s_glist[nvalid + off + mbcnt(bal)] = gm;
-    nvalid += tot;
-    __syncthreads();
-  }
+  // routing row -> LDS: its ascending prefix of groups before the own chunk
+  const int nvalid = load_routing_prefix<kThreads>(p.gidx + row * p.top_g, p.top_g, cb * 8,
+                                                   s_glist, s_wsum);
   const int ntiles = kLocalTiles + (nvalid + kGroupsPerTile - 1) / kGroupsPerTile;
 
   const T* Kbh = reinterpret_cast<const T*>(p.K) + (long long)bh * p.Scap * D;
@@ -195,6 +186,7 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
     else wait_vmcnt<0>();
     __syncthreads();   // tile ti visible to all; everyone is done with tile ti-1
     if (ti + S - 1 < ntiles) issue(ti + S - 1, gnext);
+    if constexpr (HGA_GATHER_ONLY != 0) continue;
 
     const char* kt = smem + (ti % S) * kStage;
     const char* vt = kt + kTileBytes;
@@ -295,6 +287,10 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
   }
 
   // epilogue: normalise, write O (4 consecutive elements per lane) and lse
+  if constexpr (HGA_GATHER_ONLY != 0) {
+    l_run = 0.25f;
+    m_run = 0.f;
+  }
   const float l_tot = xor_sum16_32(l_run);
   const float inv = 1.0f / l_tot;
   T* o = reinterpret_cast<T*>(p.O) + (qrow0 + qq) * D + 4 * g4;

@@ -149,13 +149,28 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(const DecP p) {
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
 
+  // the kept groups taken from the row: its longest prefix of groups before
+  // the own chunk, each above the one before it (all p.ngk entries of a row
+  // written by the routing); slots past the prefix hold no key
+  int nk = p.ngk;
+  for (int s0 = 0; s0 < p.ngk; s0 += 64) {
+    const int s = s0 + lane;
+    const int v = s < p.ngk ? gl[s] : 0;
+    const int prev = s > 0 && s < p.ngk ? gl[s - 1] : -1;
+    const uint64_t bad = __ballot(s < p.ngk && (v < 0 || v >= kGroup * p.cp || v <= prev));
+    if (bad) {
+      nk = s0 + (int)__builtin_ctzll(bad);
+      break;
+    }
+  }
+
   for (int t = wv; t < p.ntiles; t += nw) {
-    // the tile's 4 groups (-1: past the end of the key list)
+    // the tile's 4 groups (-1: no key in the slot)
     int g[kTileGroups];
 #pragma unroll
     for (int j = 0; j < kTileGroups; ++j) {
       const int s = kTileGroups * t + j;
-      g[j] = s < p.ngk ? gl[s] : (s < p.ng ? kGroup * p.cp + (s - p.ngk) : -1);
+      g[j] = s < nk ? gl[s] : s < p.ngk ? -1 : (s < p.ng ? kGroup * p.cp + (s - p.ngk) : -1);
     }
     uint4 kr[NI], vr[NI];
     load_rows<T, D, NI, RPI>(kr, Kr, g, rg, col, p.p);
@@ -189,10 +204,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(const DecP p) {
     const int gk = jt == 0 ? g[0] : jt == 1 ? g[1] : jt == 2 ? g[2] : g[3];
     const int pk = kGroup * gk + kt % kGroup;
     const float x = (gk >= 0 && pk <= p.p) ? s * p.c2 : -INFINITY;
-    // online softmax; every tile holds at least one key, so m_new is finite
+    // online softmax; a tile with no key (slots cut from a malformed row)
+    // leaves m at -inf, and the exponents are then taken against 0
     const float m_new = fmaxf(m_run, wave_max_f(x));
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float pe = __builtin_amdgcn_exp2f(x - m_new);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+    const float pe = __builtin_amdgcn_exp2f(x - m_ref);
     l_run = fmaf(l_run, alpha, wave_sum_f((c & 1) ? 0.f : pe));
     m_run = m_new;
 #pragma unroll

@@ -150,7 +150,8 @@ hga_status hga_route(const hga_shape* shape, const void* Q, const float* chunk_m
   if (st != HGA_OK) return st;
   if (!Q || !chunk_mean) return HGA_ERR_NULL;
   if (shape->top_g > 0 && (!group_idx || !group_mean)) return HGA_ERR_NULL;
-  if (shape->top_k == 0 && shape->top_g == 0 && !group_idx && !chunk_idx) return HGA_OK;
+  // no budget: both index arrays have zero entries per row, nothing to write
+  if (shape->top_k == 0 && shape->top_g == 0) return HGA_OK;
   return from_hip(hga::launch_route(dims_of(shape), Q, nullptr, false, chunk_mean, group_mean,
                                     shape->top_k > 0 ? chunk_idx : nullptr,
                                     shape->top_g > 0 ? group_idx : nullptr,
@@ -166,7 +167,8 @@ hga_status hga_route_causal(const hga_shape* shape, const void* Q, const void* Q
   if (shape->top_g > 0 && (!group_idx || !group_mean)) return HGA_ERR_NULL;
   const bool routes = shape->top_k > 0 || shape->top_g > 0;
   if (routes && shape->kv_len > shape->q_len && !Q_prev) return HGA_ERR_NULL;
-  if (!routes && !group_idx && !chunk_idx) return HGA_OK;
+  // no budget: nothing to write, and Q_prev is not read
+  if (!routes) return HGA_OK;
   return from_hip(hga::launch_route(dims_of(shape), Q, Q_prev, true, chunk_mean, group_mean,
                                     shape->top_k > 0 ? chunk_idx : nullptr,
                                     shape->top_g > 0 ? group_idx : nullptr,

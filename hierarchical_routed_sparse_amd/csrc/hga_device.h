@@ -86,6 +86,44 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
+// ----------------------------------------------------------------- routing rows
+//
+// The kept groups of a routing row, as the attention kernels read them: the
+// longest prefix of the row whose entries lie in [0, limit) and each exceed
+// the entry before them.  A row written by the routing (ascending, -1
+// padded, every group before the own chunk) is its valid entries exactly; any
+// other row is cut at its first entry that breaks the rule, so a kept group
+// is never out of range and never counted twice.  The row is copied to
+// s_glist (entries past the prefix are never read) and the prefix length is
+// returned.  Every thread of the NT-thread workgroup must call it; s_wsum
+// holds NT / 64 ints.
+template <int NT>
+__device__ __forceinline__ int load_routing_prefix(const int32_t* grow, int top_g, int limit,
+                                                   int* s_glist, int* s_wsum) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int n = top_g;
+  for (int i0 = 0; i0 < top_g; i0 += NT) {
+    const int i = i0 + tid;
+    const int gm = i < top_g ? grow[i] : -1;
+    const int prev = i > 0 && i < top_g ? grow[i - 1] : -1;
+    if (i < top_g) s_glist[i] = gm;
+    const bool bad = i < top_g && (gm < 0 || gm >= limit || gm <= prev);
+    const uint64_t bal = __ballot(bad);
+    if (lane == 0) s_wsum[wv] = bal ? i0 + 64 * wv + (int)__builtin_ctzll(bal) : top_g;
+    __syncthreads();
+    int first = top_g;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) first = min(first, s_wsum[k]);
+    __syncthreads();
+    if (first < top_g) {
+      n = first;
+      break;
+    }
+  }
+  return n;
+}
+
 // ----------------------------------------------------------------- fragments
 
 template <typename T> struct Frag;

@@ -165,6 +165,10 @@ WORKLOADS = {
                  1 / math.sqrt(128), backward=True,
                  description="bf16 causal self-attention, batch 2, 32q/8kv, D128, 4K tokens, "
                              "k8 g32, forward + backward"),
+        Workload("causal_16k", 1, 32, 8, 128, 16384, 16384, 16, 64, "bf16", 6,
+                 1 / math.sqrt(128), backward=True,
+                 description="bf16 causal self-attention over a whole 16384-token sequence, "
+                             "32q/8kv, D128, k16 g64, forward + backward"),
         Workload("decode_b16_16k", 16, 32, 8, 128, 1, 16424, 16, 64, "bf16", 5,
                  1 / math.sqrt(128),
                  description="bf16 decode: one new token per sequence at position 16423 of "

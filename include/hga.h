@@ -162,7 +162,14 @@ hga_status hga_route_causal(const hga_shape* shape, const void* Q, const void* Q
  * absolute position p of block blk attends every token of the row's kept
  * groups plus its own chunk's tokens up to and including p.
  *   group_idx  [B][Hq][q_len/64][top_g]  int32, as produced by hga_route
- *              (ascending, -1 padded, every group before the own chunk)
+ *              (ascending, -1 padded, every group before the own chunk).
+ *              The kept groups of a row are its longest prefix of entries
+ *              that lie in [0, 8 * own chunk) and each exceed the entry
+ *              before them: for a row written by hga_route, exactly its
+ *              non-negative entries.  Any other row is cut at its first entry
+ *              that breaks this rule, so no group is read out of range or
+ *              attended twice.  The backward and decode calls read rows by
+ *              the same rule.
  *   O          [B][Hq][q_len][D]         dtype
  *   lse        [B][Hq][q_len]            fp32 natural-log log-sum-exp of the
  *                                        scaled logits, nullable */
@@ -183,6 +190,7 @@ hga_status hga_attend_bwd_workspace(const hga_shape* shape, size_t* bytes);
  * (page section "What HGA does differently": the router has no weights and
  * gradients reach the same Q/K/V projections as dense attention).
  *   O, lse     outputs of hga_attend_fwd for the same inputs
+ *   group_idx  as for hga_attend_fwd (same prefix rule)
  *   dO         [B][Hq][q_len][D]   dtype
  *   dQ         [B][Hq][q_len][D]   dtype
  *   dK, dV     [B][Hkv][C][D] dtype; every position below kv_len is written
@@ -201,7 +209,9 @@ hga_status hga_attend_bwd(const hga_shape* shape, const void* Q, const void* K, 
  * whole chunk range into the workspace; hga_attend_bwd_dkdv then reads them
  * from the same workspace and computes dK and dV.  The dkdv call must follow
  * a dq call with the same inputs, on the same stream (or after it has
- * completed). */
+ * completed).  A dkdv call on a workspace that no such dq call wrote gives
+ * unspecified dK/dV values but never writes outside dK and dV: work-order
+ * entries outside the chunk range are skipped. */
 hga_status hga_attend_bwd_dq(const hga_shape* shape, const void* Q, const void* K,
                              const void* V, const void* O, const float* lse, const void* dO,
                              const int32_t* group_idx, void* dQ, void* workspace,
@@ -242,7 +252,11 @@ hga_status hga_attend_bwd_dkdv_range(const hga_shape* shape, const void* Q, cons
  *              built (hga_build_summaries with this shape)
  *   chunk_idx  [B][Hq][top_k]      int32, nullable
  *   group_idx  [B][Hq][top_g]      int32, required when top_g > 0 (written by
- *                                  the routing, read by the attention)
+ *                                  the routing, read by the attention: its
+ *                                  first min(top_g, 8 * kept chunks) entries,
+ *                                  cut at the first entry that is negative,
+ *                                  not before the own chunk or not above the
+ *                                  entry before it)
  *   O          [B][Hq][D]          dtype
  *   lse        [B][Hq]             fp32 natural-log log-sum-exp, nullable
  * Routing: the routing query is the token's query itself; the row keeps

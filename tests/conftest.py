@@ -17,3 +17,15 @@ def oracle():
     import oracle as o
     o.build(force=False)
     return o
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Keeps the routing tie-band counts of a GPU run (how many rows a near
+    tie let differ, by stage) where the run keeps its outputs."""
+    gc = sys.modules.get("gpu_common")
+    out = os.path.join(ROOT, "gpurun_out")
+    if gc is None or not gc.TIE_LOG or not os.path.isdir(out):
+        return
+    import json
+    with open(os.path.join(out, "tie_band.json"), "w") as f:
+        json.dump(gc.TIE_LOG, f, indent=1)

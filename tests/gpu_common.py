@@ -47,11 +47,14 @@ def check_routing(oracle, w, Qf, cm_o, gm_o, ci_gpu, gi_gpu, rows=None, causal=F
                   Qprev=None):
     """GPU routing vs the oracle under the near-tie rule (``causal``: the
     strictly causal variant, ``Qprev`` the 64 queries before the segment).
-    Returns the number of rows where a near tie allowed a difference."""
+    Returns the number of rows where a near tie allowed a difference; the
+    counts by stage are appended to TIE_LOG (chunk rows tolerated, group rows
+    re-derived on the GPU's chunk set, group rows tolerated)."""
+    rows = list(rows) if rows is not None else None
     ci_o, gi_o, cs, gs = oracle.route(Qf, cm_o, gm_o, w.kv_len, w.top_k, w.top_g,
                                       want_scores=True, causal=causal, Qprev=Qprev)
     tolerated = 0
-    forced = None
+    chunk_tol = 0
     B, Hq, nblk = ci_gpu.shape[:3]
     for idx in (rows if rows is not None else np.ndindex(B, Hq, nblk)):
         a, b = ci_gpu[idx], ci_o[idx]
@@ -62,8 +65,12 @@ def check_routing(oracle, w, Qf, cm_o, gm_o, ci_gpu, gi_gpu, rows=None, causal=F
             ok, exact = tie_band_ok(a, b, cs[idx], w.top_k)
             assert ok, f"chunk routing differs beyond the tie band at {idx}: {a} vs {b}"
             tolerated += 1
-    # groups: against the oracle's choice given the GPU's chunk sets
+    chunk_tol = tolerated
+    # groups: against the oracle's choice given the GPU's chunk sets (the
+    # oracle's forced-chunk branch, pinned on the CPU)
+    forced_rows = 0
     if not np.array_equal(ci_gpu, ci_o):
+        forced_rows = int(np.any(ci_gpu != ci_o, axis=-1).sum())
         _, gi_o, _, gs = oracle.route(Qf, cm_o, gm_o, w.kv_len, w.top_k, w.top_g,
                                       forced_chunk_idx=ci_gpu, want_scores=True, causal=causal,
                                       Qprev=Qprev)
@@ -75,7 +82,16 @@ def check_routing(oracle, w, Qf, cm_o, gm_o, ci_gpu, gi_gpu, rows=None, causal=F
             ok, exact = tie_band_ok(a, b, gs[idx], w.top_g)
             assert ok, f"group routing differs beyond the tie band at {idx}: {a} vs {b}"
             tolerated += 1
+    nrows = int(np.prod(ci_gpu.shape[:3])) if rows is None else len(rows)
+    TIE_LOG.append({"case": w.name, "rows": nrows, "chunk_rows_tolerated": chunk_tol,
+                    "group_rows_on_gpu_chunk_set": forced_rows,
+                    "group_rows_tolerated": tolerated - chunk_tol})
     return tolerated
+
+
+# per-call counts of check_routing, for the tie-band summary the full-size
+# routing test writes when a run keeps a gpurun_out/ directory
+TIE_LOG = []
 
 
 def assert_close(got, ref, dtype, what):

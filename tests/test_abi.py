@@ -114,7 +114,7 @@ def test_status_strings(lib):
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(hga, "LIB_PATH", str(tmp_path / "missing.so"))
-    monkeypatch.setattr(hga, "_lib", None)
+    monkeypatch.setattr(hga, "_libs", {})
     with pytest.raises(hga.HGAError):
         hga.hga_abi_version()
 
@@ -198,3 +198,19 @@ def test_decode_halves_argument_errors(lib):
     assert lib.hga_decode_attend(ctypes.byref(s), 16, None, 16, 16, 16, 16, None) == 1  # K
     assert lib.hga_decode_attend(ctypes.byref(s), 16, 16, 16, 16, None, 16, None) == 1  # O
     assert lib.hga_decode_attend(ctypes.byref(_ok_shape()), 16, 16, 16, 16, 16, 16, None) == 2
+
+
+def test_zero_budget_routing_launches_nothing(lib):
+    """top_k == top_g == 0: both index arrays have no entries, so the routing
+    calls return before any launch.  In particular hga_route_causal with
+    kv_len > q_len and Q_prev NULL does not read Q_prev (the pointers below
+    are not device memory: a launch would have to touch them).  Host only."""
+    s = _ok_shape(top_k=0, top_g=0)
+    fake = ctypes.c_void_p(16)
+    lib.hga_route_causal.argtypes = [ctypes.c_void_p] * 8
+    lib.hga_route.argtypes = [ctypes.c_void_p] * 7
+    assert lib.hga_route_causal(ctypes.byref(s), fake, None, fake, None, fake, fake, None) == 0
+    assert lib.hga_route(ctypes.byref(s), fake, fake, None, fake, fake, None) == 0
+    # with a budget, the missing Q_prev is still an argument error
+    s = _ok_shape(top_k=4, top_g=0)
+    assert lib.hga_route_causal(ctypes.byref(s), fake, None, fake, None, fake, None, None) == 1

@@ -49,11 +49,31 @@ def test_training_step_work_per_unit():
     # routing: the block's 64 bf16 query rows, then once the means, then indices
     means = 8 * (256 + 2048) * 128 * 4
     assert work["route"] == ("hbm", 32 * 2048 * 128 * 2 + means + 32 * 32 * (16 + 64) * 4)
-    # 2 flops per multiply-add, D = 128 per product and pair
+    # 2 flops per multiply-add, D = 128 per product and pair: the forward's two
+    # products; the backward's five, three (Q.K^T, dO.V^T, dS.K) for dQ and
+    # two (P^T.dO, dS^T.Q) for dK/dV, 10 D per pair in all
     assert work["attend_fwd"] == ("mfma", 2 * 2 * 128 * pairs)
     assert work["attend_bwd_dq"] == ("mfma", 3 * 2 * 128 * pairs)
-    assert work["attend_bwd_dkdv"] == ("mfma", 4 * 2 * 128 * pairs)
-    assert work["attend_bwd_dkdv"][1] == 36_540_776_448
+    assert work["attend_bwd_dkdv"] == ("mfma", 2 * 2 * 128 * pairs)
+    assert work["attend_bwd_dq"][1] + work["attend_bwd_dkdv"][1] == 10 * 128 * pairs
+    assert work["attend_bwd_dkdv"][1] == 18_270_388_224
+
+
+def test_executed_work_counts_tiles_and_slices():
+    """Executed MFMA flops from the kernels' tiling, restated by brute force on
+    a small routing: forward and dQ walk 2 own-chunk tiles plus one 32-key
+    tile per 4 kept groups; dK/dV works on every 16-key slice (group pair)
+    with a kept group, plus the 4 slices of the own chunk."""
+    gi = np.full((1, 2, 2, 6), -1, dtype=np.int32)
+    gi[0, 0, 0, :5] = [0, 1, 2, 9, 17]      # pairs {0, 1, 4, 8}; 2 group tiles
+    gi[0, 1, 1, :2] = [3, 40]               # pairs {1, 20}; 1 group tile
+    D = 64
+    ex = bench.executed_work(gi, D)
+    tiles = (2 + 2) + (2 + 0) + (2 + 0) + (2 + 1)
+    assert ex["attend_fwd"] == tiles * 32 * 64 * 4 * D
+    assert ex["attend_bwd_dq"] == tiles * 32 * 64 * 6 * D
+    slices = (4 + 4) + 4 + 4 + (2 + 4)
+    assert ex["attend_bwd_dkdv"] == slices * 16 * 64 * 8 * D
 
 
 def test_decode_work_per_row():

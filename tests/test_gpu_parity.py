@@ -292,3 +292,73 @@ def test_maximum_kv_length(oracle, dtype):
     assert_close(f64(dQ), dQ_o, dtype, "dQ")
     assert_close(f64(dK), dK_o, dtype, "dK")
     assert_close(f64(dV), dV_o, dtype, "dV")
+
+
+# ------------------------------------------------------------------ boundary extremes
+
+EXTREMES = {
+    # block routing at the largest budgets: 64 chunks (the 8-slot group select),
+    # 512 groups (routing-row slots 256..511, the second pass of the row load)
+    # out of 66 and 67 candidate chunks
+    "k64_g512_bf16": syn.Workload("k64_g512_bf16", 1, 2, 1, 64, 128, 4352, 64, 512, "bf16",
+                                  81, 0.125, backward=True),
+    "k64_g512_fp32": syn.Workload("k64_g512_fp32", 1, 2, 1, 64, 128, 4352, 64, 512, "fp32",
+                                  82, 0.3, backward=True),
+    # more than 1024 routing rows per kv head (8 query heads x 129 blocks = 1032):
+    # the dK/dV entry list is built in two passes over the rows
+    "rows1032_bf16": syn.Workload("rows1032_bf16", 1, 8, 1, 64, 8256, 8256, 2, 8, "bf16", 83,
+                                  0.125, backward=True),
+}
+
+
+@pytest.mark.parametrize("name", list(EXTREMES))
+def test_boundary_extremes_full_parity(oracle, name):
+    """Element-by-element parity at the limits the boundary accepts."""
+    _full_parity(oracle, EXTREMES[name])
+
+
+def test_causal_16k_full_size(oracle):
+    """The full 16384-token causal self-attention (32q/8kv, D128, k16 g64):
+    summaries and routing of every row; the forward of three sampled query
+    heads on their blocks 128..255; the backward of one kv head with its four
+    query heads on blocks 224..255.  A query block attends only keys at or
+    before its own chunk, so the oracle run on the rows of blocks >= c (a
+    segment at the end of the same history) gives those rows' O, lse and dQ
+    exactly, and the complete dK, dV of every key in chunks >= c."""
+    w = W["causal_16k"]
+    print(f"[case] full {w.name}", flush=True)
+    x = syn.make_inputs(w, with_grad_output=True)
+    s, x, t, out = run_forward(w, x)
+    Kf = syn.to_f64(x["K"], w.dtype)
+    cm_o, gm_o = oracle.summaries(Kf)
+    np.testing.assert_allclose(f64(out["chunk_mean"]), cm_o, atol=1e-5, rtol=1e-5)
+    np.testing.assert_allclose(f64(out["group_mean"]), gm_o, atol=1e-5, rtol=1e-5)
+    tolerated = check_routing(oracle, w, syn.to_f64(x["Q"], w.dtype), cm_o, gm_o,
+                              out["chunk_idx"].cpu().numpy(), out["group_idx"].cpu().numpy())
+    print(f"[routing] {w.name}: rows inside the near-tie band: {tolerated}", flush=True)
+    del Kf, cm_o, gm_o
+    r = w.n_q_heads // w.n_kv_heads
+    gi = out["group_idx"].cpu().numpy()
+    O, lse = f64(out["O"]), f64(out["lse"])
+    c = 128
+    qs = slice(64 * c, w.q_len)
+    for hq in (0, 13, 31):
+        hkv = hq // r
+        O_o, lse_o = oracle.attend_fwd(syn.to_f64(x["Q"][:, hq:hq + 1, qs], w.dtype),
+                                       syn.to_f64(x["K"][:, hkv:hkv + 1], w.dtype),
+                                       syn.to_f64(x["V"][:, hkv:hkv + 1], w.dtype),
+                                       gi[:, hq:hq + 1, c:])
+        assert_close(O[:, hq:hq + 1, qs], O_o, w.dtype, f"O[{hq}]")
+        assert_close(lse[:, hq:hq + 1, qs], lse_o, w.dtype, f"lse[{hq}]")
+    dQ, dK, dV = hga.backward(s, t["Q"], t["K"], t["V"], out["O"], out["lse"], t["dO"],
+                              out["group_idx"])
+    torch.cuda.synchronize()
+    hkv, c = 3, 224
+    hs, qs, ks = slice(hkv * r, (hkv + 1) * r), slice(64 * c, w.q_len), slice(64 * c, w.kv_len)
+    dQ_o, dK_o, dV_o = oracle.attend_bwd(syn.to_f64(x["Q"][:, hs, qs], w.dtype),
+                                         syn.to_f64(x["K"][:, hkv:hkv + 1], w.dtype),
+                                         syn.to_f64(x["V"][:, hkv:hkv + 1], w.dtype),
+                                         gi[:, hs, c:], syn.to_f64(x["dO"][:, hs, qs], w.dtype))
+    assert_close(f64(dQ)[:, hs, qs], dQ_o, w.dtype, "dQ")
+    assert_close(f64(dK)[:, hkv:hkv + 1, ks], dK_o[:, :, ks], w.dtype, "dK")
+    assert_close(f64(dV)[:, hkv:hkv + 1, ks], dV_o[:, :, ks], w.dtype, "dV")

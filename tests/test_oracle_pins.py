@@ -267,3 +267,82 @@ def test_attended_pairs_constant_per_block(oracle):
         nrows = 2 * 4
         assert oracle.attended_pairs(gi) == nrows * (64 * 8 * 16 + 64 * 65 // 2)
         assert oracle.attended_pairs(gi) == hga_mask(gi, 256, Skv).sum()
+
+
+# ---------------------------------------------------------------- forced chunk sets
+
+def _numpy_groups_on_chunks(qbar, K, chunks, top_g, G=8):
+    """Independent joint top-g over the groups of a given chunk set: group means
+    from a numpy reshape, scores q.mean, full sort on (-score, index), kept
+    groups ascending, -1 padded."""
+    cand = [8 * c + t for c in chunks if c >= 0 for t in range(8)]
+    gmean = K.reshape(-1, G, K.shape[-1]).mean(axis=1)
+    scored = sorted(((-float(qbar @ gmean[x]), x) for x in cand))
+    kept = sorted(x for _, x in scored[:min(top_g, len(cand))])
+    return kept + [-1] * (top_g - len(kept))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_route_forced_chunks_match_numpy(oracle, causal):
+    """With forced chunk sets (here random sets, not the top-k), the oracle's
+    group stage equals an independent numpy joint top-g over those chunks'
+    groups, for the block routing query and for the strictly causal one (the
+    mean of the 64 queries before the block).  This is the branch the GPU tests
+    use when a near tie lets the GPU keep a different chunk set."""
+    B, Hq, Hkv, Sq, Skv, D, k, g = 1, 4, 2, 256, 768, 16, 4, 13
+    Q = _rand((B, Hq, Sq, D))
+    K = _rand((B, Hkv, Skv, D))
+    Qprev = _rand((B, Hq, 64, D)) if causal else None
+    cm, gm = oracle.summaries(K)
+    nblk, q0, r = Sq // 64, Skv - Sq, Hq // Hkv
+    frng = np.random.default_rng(7)
+    forced = np.full((B, Hq, nblk, k), -1, dtype=np.int32)
+    for h in range(Hq):
+        for blk in range(nblk):
+            cb = q0 // 64 + blk
+            n = int(frng.integers(0, k + 1))
+            forced[0, h, blk, :n] = np.sort(frng.choice(cb, size=n, replace=False))
+    ci, gi = oracle.route(Q, cm, gm, Skv, k, g, forced_chunk_idx=forced, causal=causal,
+                          Qprev=Qprev)
+    assert np.array_equal(ci, forced)
+    for h in range(Hq):
+        for blk in range(nblk):
+            if not causal:
+                src = Q[0, h, blk * 64:(blk + 1) * 64]
+            elif blk > 0:
+                src = Q[0, h, (blk - 1) * 64:blk * 64]
+            else:
+                src = Qprev[0, h]
+            want = _numpy_groups_on_chunks(src.mean(axis=0), K[0, h // r], forced[0, h, blk], g)
+            assert gi[0, h, blk].tolist() == want, (h, blk)
+
+
+def test_route_forced_chunk_outside_candidates_rejected(oracle):
+    Q, K = _rand((1, 1, 64, 8)), _rand((1, 1, 256, 8))
+    cm, gm = oracle.summaries(K)
+    forced = np.array([[[[1, 3]]]], dtype=np.int32)   # chunk 3 is the block's own chunk
+    with pytest.raises(ValueError):
+        oracle.route(Q, cm, gm, 256, 2, 4, forced_chunk_idx=forced)
+
+
+def test_decode_forced_chunks_match_numpy(oracle):
+    """The decode form with forced chunk sets: groups equal the numpy joint
+    top-g over the forced chunks' groups, scored with the token's query."""
+    B, Hq, Hkv, L, D, k, g = 2, 2, 1, 600, 16, 3, 11
+    Q = _rand((B, Hq, D))
+    K = _rand((B, Hkv, L, D))
+    V = _rand((B, Hkv, L, D))
+    cm, gm = oracle.summaries(K[:, :, :64 * (L // 64)])
+    cp = (L - 1) // 64
+    frng = np.random.default_rng(11)
+    forced = np.full((B, Hq, k), -1, dtype=np.int32)
+    for b in range(B):
+        for h in range(Hq):
+            n = int(frng.integers(0, k + 1))
+            forced[b, h, :n] = np.sort(frng.choice(cp, size=n, replace=False))
+    ci, gi, O, lse = oracle.decode(Q, K, V, cm, gm, k, g, forced_chunk_idx=forced)
+    assert np.array_equal(ci, forced)
+    for b in range(B):
+        for h in range(Hq):
+            want = _numpy_groups_on_chunks(Q[b, h], K[b, 0, :64 * cp], forced[b, h], g)
+            assert gi[b, h].tolist() == want, (b, h)
