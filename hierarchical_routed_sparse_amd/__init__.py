@@ -25,7 +25,7 @@ import os
 __all__ = [
     "HGAError", "HgaShape", "make_shape", "lib_path", "hga_abi_version", "hga_validate_shape",
     "hga_build_summaries", "hga_route", "hga_route_causal", "hga_attend_fwd", "hga_attend_bwd_workspace",
-    "hga_attend_bwd", "hga_attend_bwd_dq", "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range",
+    "hga_attend_bwd", "hga_attend_bwd_noalloc", "hga_attend_bwd_dq", "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range",
     "hga_validate_decode_shape", "hga_decode", "hga_decode_route", "hga_decode_attend",
     "hga_decode_route_causal",
     "forward", "backward", "decode",
@@ -96,6 +96,7 @@ def _load(path: str = None):
     lib.hga_attend_fwd.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.hga_attend_bwd_workspace.argtypes = [_SP, ctypes.POINTER(sz)]
     lib.hga_attend_bwd.argtypes = [_SP] + [_vp] * 11 + [sz, _vp]
+    lib.hga_attend_bwd_noalloc.argtypes = [_SP] + [_vp] * 11
     lib.hga_attend_bwd_dq.argtypes = [_SP] + [_vp] * 9 + [sz, _vp]
     lib.hga_attend_bwd_dkdv.argtypes = [_SP] + [_vp] * 9 + [sz, _vp]
     lib.hga_attend_bwd_dkdv_range.argtypes = [_SP] + [_vp] * 6 + [i32, i32] + [_vp] * 3 + [sz, _vp]
@@ -106,7 +107,8 @@ def _load(path: str = None):
     lib.hga_decode_route_causal.argtypes = [_SP] + [_vp] * 6
     for name in ("hga_validate_shape", "hga_validate_decode_shape", "hga_decode", "hga_route_causal",
                  "hga_decode_route", "hga_decode_attend", "hga_decode_route_causal", "hga_build_summaries", "hga_route", "hga_attend_fwd",
-                 "hga_attend_bwd_workspace", "hga_attend_bwd", "hga_attend_bwd_dq",
+                 "hga_attend_bwd_workspace", "hga_attend_bwd", "hga_attend_bwd_noalloc",
+                 "hga_attend_bwd_dq",
                  "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range"):
         getattr(lib, name).restype = ctypes.c_int
     _libs[path] = lib
@@ -304,6 +306,20 @@ def hga_attend_bwd(shape, Q, K, V, O, lse, dO, group_idx, dQ, dK, dV, workspace,
         _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
         _ptr(dQ, "dQ", dt, sz["q"]), _ptr(dK, "dK", dt, sz["kv"]), _ptr(dV, "dV", dt, sz["kv"]),
         wp, wb, _stream(stream)), "hga_attend_bwd")
+
+
+def hga_attend_bwd_noalloc(shape, Q, K, V, O, lse, dO, group_idx, dQ, dK, dV, stream=None):
+    """hga_attend_bwd with the workspace held by the library (for callers that
+    cannot allocate); calls that overlap on one GPU race on it."""
+    import torch
+    sz, dt = _sizes(shape), _elt_dtype(shape)
+    _check(_load().hga_attend_bwd_noalloc(
+        ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"], host_ok=True),
+        _ptr(V, "V", dt, sz["kv"], host_ok=True), _ptr(O, "O", dt, sz["q"]),
+        _ptr(lse, "lse", torch.float32, sz["lse"]), _ptr(dO, "dO", dt, sz["q"]),
+        _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        _ptr(dQ, "dQ", dt, sz["q"]), _ptr(dK, "dK", dt, sz["kv"]), _ptr(dV, "dV", dt, sz["kv"]),
+        _stream(stream)), "hga_attend_bwd_noalloc")
 
 
 def hga_attend_bwd_dq(shape, Q, K, V, O, lse, dO, group_idx, dQ, workspace, stream=None):

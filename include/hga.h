@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 5
+#define HGA_ABI_VERSION 6
 #define HGA_CHUNK 64      /* tokens per chunk (the page's 64-token chunks) */
 #define HGA_GROUP 8       /* tokens per group (the page's 8-token groups)  */
 #define HGA_QBLOCK 64     /* queries per routing block                      */
@@ -202,6 +202,24 @@ hga_status hga_attend_bwd(const hga_shape* shape, const void* Q, const void* K, 
                           const void* O, const float* lse, const void* dO,
                           const int32_t* group_idx, void* dQ, void* dK, void* dV,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* hga_attend_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and results, with the workspace taken from a device
+ * array of HGA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on (until the process ends).  The call allocates nothing; the caller
+ * still passes every input and output as for hga_attend_bwd.
+ * Returns HGA_ERR_WORKSPACE when hga_attend_bwd_workspace(shape) exceeds
+ * HGA_NOALLOC_SCRATCH_BYTES, and HGA_ERR_HIP when the array's device address
+ * cannot be resolved.  All calls on one GPU share that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other threads) race on it and
+ * must be serialised by the caller.  The array keeps the last call's contents;
+ * nothing in it needs clearing between calls. */
+#define HGA_NOALLOC_SCRATCH_BYTES (16u << 20)
+hga_status hga_attend_bwd_noalloc(const hga_shape* shape, const void* Q, const void* K,
+                                  const void* V, const void* O, const float* lse,
+                                  const void* dO, const int32_t* group_idx, void* dQ, void* dK,
+                                  void* dV, void* stream);
 
 /* The two halves of hga_attend_bwd, for callers that schedule them apart.
  * hga_attend_bwd_dq computes dQ and writes the row statistics
