@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--workload", default="segment_2k_over_16k",
                     help="segment_2k_over_16k (the headline), causal_16k, fwd_bwd_b2_4k, "
                          "qwen3_8b_2k, segment_2k_over_64k_ties, tiny_fp32_1k")
+    ap.add_argument("--side-by-side-bwd", action="store_true",
+                    help="time the backward as the preparation pass, then dQ on a second "
+                         "stream beside dK/dV (default: dQ, then dK/dV on one stream)")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time the forward step only (summaries, routing, attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -728,12 +731,29 @@ def main():
 
     def step(ev=None):
         # every call launches on the current stream (the capture stream inside
-        # a graph capture)
+        # a graph capture); the backward in sequence: dQ (writing the dK/dV
+        # metadata into the workspace), then dK/dV
         stream = torch.cuda.current_stream()
         for i, p in enumerate(phases):
             if ev: ev[i].record(stream)
             calls[p]()
         if ev: ev[len(phases)].record(stream)
+
+    side = torch.cuda.Stream()
+
+    def step_side_by_side():
+        # the backward's metadata from its preparation pass, then dQ on a
+        # second stream beside dK/dV on the first (forked and joined by events,
+        # which a graph capture records as its dependencies)
+        main = torch.cuda.current_stream()
+        for p in phases[:3]:
+            calls[p]()
+        hga.hga_attend_bwd_prep(s, O, t["dO"], gi, ws)
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            hga.hga_attend_bwd_dq(s, t["Q"], t["K"], t["V"], O, lse, t["dO"], gi, dQ, None)
+        calls["attend_bwd_dkdv"]()
+        main.wait_stream(side)
 
     for _ in range(args.warmup):
         step()
@@ -752,8 +772,16 @@ def main():
     eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     phase_ms = {p: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
                 for i, p in enumerate(phases)}
-    # the timed region: the step replayed from a HIP graph
-    ms_step = timed_replays(graph_of(step), args.steps, args.warmup)
+    # the timed region: the step replayed from a HIP graph; with
+    # --side-by-side-bwd, dQ and dK/dV run side by side after the
+    # preparation pass
+    ms_serial = timed_replays(graph_of(step), args.steps, args.warmup)
+    ms_step = ms_serial
+    if not fwd_only and args.side_by_side_bwd:
+        for _ in range(args.warmup):
+            step_side_by_side()
+        torch.cuda.synchronize()
+        ms_step = timed_replays(graph_of(step_side_by_side), args.steps, args.warmup)
     pairs = attended_pairs(gi)
     work = algorithmic_work(w, pairs)
     executed = executed_work(gi.cpu().numpy(), w.head_dim)
@@ -777,6 +805,11 @@ def main():
     # kernel-only durations of every phase (back-to-back launches in a graph)
     for p in phases:
         phase_rep[p]["kernel_us"] = round(kernel_us(calls[p]), 2)
+    if not fwd_only:
+        phase_rep["attend_bwd_prep"] = {"kernel_us": round(kernel_us(
+            lambda: hga.hga_attend_bwd_prep(s, O, t["dO"], gi, ws)), 2),
+            "note": "delta, group-mask map and dK/dV work order for the side-by-side "
+                    "backward (the serial backward has dQ write them)"}
     dom = max(phases, key=lambda p: phase_rep[p]["kernel_us"])
     kind, amount = work[dom]
     dom_us = phase_rep[dom]["kernel_us"]
@@ -848,6 +881,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "one_stream_ms_per_step": ms_serial,
         "eager_ms_per_step": eager_ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -855,6 +889,9 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded clustered keys, N(0,1)/sqrt(128) queries and values)",
         "config": {
+            "backward_schedule": None if fwd_only else (
+                "prep, then dQ on a second stream beside dK/dV" if args.side_by_side_bwd
+                else "dQ, then dK/dV on one stream"),
             "workload": f"{w.name} {what}" + (", strictly causal routing" if args.causal else ""),
             "batch": w.batch, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "q_len": w.q_len, "kv_len": w.kv_len,

@@ -25,7 +25,7 @@ import os
 __all__ = [
     "HGAError", "HgaShape", "make_shape", "lib_path", "hga_abi_version", "hga_validate_shape",
     "hga_build_summaries", "hga_route", "hga_route_causal", "hga_attend_fwd", "hga_attend_bwd_workspace",
-    "hga_attend_bwd", "hga_attend_bwd_noalloc", "hga_attend_bwd_dq", "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range",
+    "hga_attend_bwd", "hga_attend_bwd_noalloc", "hga_attend_bwd_prep", "hga_attend_bwd_dq", "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range",
     "hga_validate_decode_shape", "hga_decode", "hga_decode_route", "hga_decode_attend",
     "hga_decode_route_causal",
     "forward", "backward", "decode",
@@ -97,6 +97,7 @@ def _load(path: str = None):
     lib.hga_attend_bwd_workspace.argtypes = [_SP, ctypes.POINTER(sz)]
     lib.hga_attend_bwd.argtypes = [_SP] + [_vp] * 11 + [sz, _vp]
     lib.hga_attend_bwd_noalloc.argtypes = [_SP] + [_vp] * 11
+    lib.hga_attend_bwd_prep.argtypes = [_SP] + [_vp] * 4 + [sz, _vp]
     lib.hga_attend_bwd_dq.argtypes = [_SP] + [_vp] * 9 + [sz, _vp]
     lib.hga_attend_bwd_dkdv.argtypes = [_SP] + [_vp] * 9 + [sz, _vp]
     lib.hga_attend_bwd_dkdv_range.argtypes = [_SP] + [_vp] * 6 + [i32, i32] + [_vp] * 3 + [sz, _vp]
@@ -108,6 +109,7 @@ def _load(path: str = None):
     for name in ("hga_validate_shape", "hga_validate_decode_shape", "hga_decode", "hga_route_causal",
                  "hga_decode_route", "hga_decode_attend", "hga_decode_route_causal", "hga_build_summaries", "hga_route", "hga_attend_fwd",
                  "hga_attend_bwd_workspace", "hga_attend_bwd", "hga_attend_bwd_noalloc",
+                 "hga_attend_bwd_prep",
                  "hga_attend_bwd_dq",
                  "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range"):
         getattr(lib, name).restype = ctypes.c_int
@@ -322,10 +324,21 @@ def hga_attend_bwd_noalloc(shape, Q, K, V, O, lse, dO, group_idx, dQ, dK, dV, st
         _stream(stream)), "hga_attend_bwd_noalloc")
 
 
-def hga_attend_bwd_dq(shape, Q, K, V, O, lse, dO, group_idx, dQ, workspace, stream=None):
+def hga_attend_bwd_prep(shape, O, dO, group_idx, workspace, stream=None):
     import torch
     sz, dt = _sizes(shape), _elt_dtype(shape)
     wp, wb = _ws(workspace)
+    _check(_load().hga_attend_bwd_prep(
+        ctypes.byref(shape), _ptr(O, "O", dt, sz["q"]), _ptr(dO, "dO", dt, sz["q"]),
+        _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True), wp, wb,
+        _stream(stream)), "hga_attend_bwd_prep")
+
+
+def hga_attend_bwd_dq(shape, Q, K, V, O, lse, dO, group_idx, dQ, workspace, stream=None):
+    """``workspace`` None: dQ only (no workspace written)."""
+    import torch
+    sz, dt = _sizes(shape), _elt_dtype(shape)
+    wp, wb = _ws(workspace) if workspace is not None else (None, 0)
     _check(_load().hga_attend_bwd_dq(
         ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"], host_ok=True),
         _ptr(V, "V", dt, sz["kv"], host_ok=True), _ptr(O, "O", dt, sz["q"]),

@@ -132,6 +132,31 @@ __device__ __forceinline__ void dq_order_block(const DqP& p, int bh, int* s_mem)
   }
 }
 
+// The routing row's entry of the group-mask map: byte c = mask of the row's
+// kept groups in chunk c (bit t = group 8c + t), for every chunk of the
+// history, from the row's kept groups in s_glist (ascending, nvalid of them).
+// s_cm: nchunks bytes of LDS.  Every thread of the workgroup must call it.
+template <typename P>
+__device__ __forceinline__ void write_cmask_row(const P& p, long long row, int nvalid,
+                                                const int* s_glist, uint8_t* s_cm) {
+  const int tid = threadIdx.x;
+  const int nch = p.Skv / kChunk;
+  for (int i = tid; i < nch; i += kThreads) s_cm[i] = 0;
+  __syncthreads();
+  // the last kept group of each chunk (the list is ascending) ORs the run
+  for (int i = tid; i < nvalid; i += kThreads) {
+    const int ch = s_glist[i] >> 3;
+    if (i + 1 == nvalid || (s_glist[i + 1] >> 3) != ch) {
+      uint32_t m = 0;
+      for (int j = i; j >= 0 && (s_glist[j] >> 3) == ch; --j) m |= 1u << (s_glist[j] & 7);
+      s_cm[ch] = (uint8_t)m;
+    }
+  }
+  __syncthreads();
+  uint8_t* out = p.cmask + row * nch;
+  for (int i = tid; i < nch; i += kThreads) out[i] = s_cm[i];
+}
+
 // bf16: the register budget is held to four wavefronts per SIMD (4
 // workgroups per CU, the most the LDS stages allow): the kernel is bound by
 // latency more than by issue, so the extra resident wavefronts pay for the
@@ -162,7 +187,8 @@ void attend_bwd_dq_kernel(const DqP p) {
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  // workgroups past the dQ work compute the dK/dV work order
+  // workgroups past the dQ work compute the dK/dV work order (launched only
+  // with a workspace)
   static_assert(S * kStage >= (2048 + 256 + 4) * (int)sizeof(int), "order scratch in smem");
   if ((int)blockIdx.x >= p.nwork) {
     dq_order_block(p, (int)blockIdx.x - p.nwork, reinterpret_cast<int*>(smem));
@@ -363,29 +389,15 @@ void attend_bwd_dq_kernel(const DqP p) {
     }
   }
 
-  // stores only after the tile pipeline: its vmcnt waits count direct loads only
-  if (g4 == 0) p.delta[qrow0 + qq] = delta;
+  // stores only after the tile pipeline: its vmcnt waits count direct loads
+  // only (delta and the map are written here only when a workspace is given)
+  if (p.delta && g4 == 0) p.delta[qrow0 + qq] = delta;
 
-  // the row of the group-mask map: byte c = mask of the kept groups of chunk c
-  // (built in LDS, the stage buffers being free once every wave is past them)
-  {
+  // the row of the group-mask map (built in LDS, the stage buffers being free
+  // once every wave is past them)
+  if (p.cmask) {
     __syncthreads();
-    const int nch = p.Skv / kChunk;
-    uint8_t* s_cm = reinterpret_cast<uint8_t*>(smem);
-    for (int i = tid; i < nch; i += kThreads) s_cm[i] = 0;
-    __syncthreads();
-    // the last kept group of each chunk (the list is ascending) ORs the run
-    for (int i = tid; i < nvalid; i += kThreads) {
-      const int ch = s_glist[i] >> 3;
-      if (i + 1 == nvalid || (s_glist[i + 1] >> 3) != ch) {
-        uint32_t m = 0;
-        for (int j = i; j >= 0 && (s_glist[j] >> 3) == ch; --j) m |= 1u << (s_glist[j] & 7);
-        s_cm[ch] = (uint8_t)m;
-      }
-    }
-    __syncthreads();
-    uint8_t* out = p.cmask + (long long)row * nch;
-    for (int i = tid; i < nch; i += kThreads) out[i] = s_cm[i];
+    write_cmask_row(p, row, nvalid, s_glist, reinterpret_cast<uint8_t*>(smem));
   }
   T* dq = reinterpret_cast<T*>(p.dQ) + (qrow0 + qq) * D + 4 * g4;
   const float sc = p.scale;
@@ -394,10 +406,59 @@ void attend_bwd_dq_kernel(const DqP p) {
     store4(dq + 16 * dd, dqacc[dd][0] * sc, dqacc[dd][1] * sc, dqacc[dd][2] * sc, dqacc[dd][3] * sc);
 }
 
+// The backward's preparation pass, for callers that run dQ and dK/dV side by
+// side: per routing row, delta = rowsum(dO * O) and the row's entry of the
+// group-mask map; per (b, kv head), the dK/dV work order (dq_order_block).
+// These are what the dQ kernel otherwise writes into the workspace, computed
+// the same way, so dK/dV results are bitwise the same after either.
 template <typename T, int D>
-hipError_t run_dq(const Dims& d, const void* Q, const void* K, const void* V, const void* O,
-                  const float* lse, const void* dO, const int32_t* gi, void* dQ, float* delta,
-                  uint8_t* cmask, int32_t* order, hipStream_t s) {
+__global__ __launch_bounds__(kThreads) void attend_bwd_prep_kernel(const DqP p) {
+  constexpr int kMaxRange = 2048;
+  __shared__ __attribute__((aligned(16))) int s_mem[kMaxRange + 256 + 4];
+  __shared__ int s_glist[kMaxTopG];
+  __shared__ int s_wsum[4];
+  if ((int)blockIdx.x >= p.nwork) {
+    dq_order_block(p, (int)blockIdx.x - p.nwork, s_mem);
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int w = xcd_remap(blockIdx.x, p.nwork);
+  const int r = p.Hq / p.Hkv;
+  const int per_bh = r * p.nblk;
+  const int bh = w / per_bh, rem = w % per_bh;
+  const int blk = rem / r, hql = rem % r;
+  const int b = bh / p.Hkv, hkv = bh % p.Hkv, hq = hkv * r + hql;
+  const int cb = p.q0 / kChunk + blk;
+  const long long row = ((long long)b * p.Hq + hq) * p.nblk + blk;
+  const long long qrow0 = ((long long)b * p.Hq + hq) * p.Sq + (long long)blk * kChunk;
+  const int qq = 16 * wv + l16;
+  // delta of this lane's query, summed in the dQ kernel's order
+  {
+    const long long off = (qrow0 + qq) * D + 8 * g4;
+    const T* go = reinterpret_cast<const T*>(p.dO) + off;
+    const T* o = reinterpret_cast<const T*>(p.O) + off;
+    Frag<T> df[D / 32], of[D / 32];
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      load_frag(df[s], go + 32 * s);
+      load_frag(of[s], o + 32 * s);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) part += frag_dot(df[s], of[s]);
+    const float delta = xor_sum16_32(part);
+    if (g4 == 0) p.delta[qrow0 + qq] = delta;
+  }
+  const int nvalid = load_routing_prefix<kThreads>(p.gidx + row * p.top_g, p.top_g, cb * 8,
+                                                   s_glist, s_wsum);
+  write_cmask_row(p, row, nvalid, s_glist, reinterpret_cast<uint8_t*>(s_mem));
+}
+
+template <typename T, int D>
+DqP dq_params(const Dims& d, const void* Q, const void* K, const void* V, const void* O,
+              const float* lse, const void* dO, const int32_t* gi, void* dQ, float* delta,
+              uint8_t* cmask, int32_t* order) {
   DqP p;
   p.Q = Q; p.K = K; p.V = V; p.O = O; p.lse = lse; p.dO = dO; p.gidx = gi; p.dQ = dQ;
   p.delta = delta; p.cmask = cmask; p.order = order;
@@ -405,13 +466,31 @@ hipError_t run_dq(const Dims& d, const void* Q, const void* K, const void* V, co
   p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.Sq = d.Sq; p.Skv = d.Skv; p.Scap = d.Scap; p.q0 = d.q0;
   p.nblk = d.nblk; p.top_g = d.top_g; p.scale = d.scale;
   p.nwork = d.B * d.Hq * d.nblk;
+  return p;
+}
+
+template <typename T, int D>
+hipError_t run_dq(const Dims& d, const void* Q, const void* K, const void* V, const void* O,
+                  const float* lse, const void* dO, const int32_t* gi, void* dQ, float* delta,
+                  uint8_t* cmask, int32_t* order, hipStream_t s) {
+  const DqP p = dq_params<T, D>(d, Q, K, V, O, lse, dO, gi, dQ, delta, cmask, order);
   constexpr int TK = HGA_DQ_TILE;
   constexpr int kStageBytes = 2 * TK * D * (int)sizeof(T);
   constexpr int S0 = HGA_DQ_STAGES;
   constexpr int S = S0 * kStageBytes <= 128 * 1024 ? S0 : (128 * 1024) / kStageBytes;
   static_assert(S >= 2, "at least two stages");
-  // + one workgroup per (b, kv head) for the dK/dV work order
-  attend_bwd_dq_kernel<T, D, TK, S><<<p.nwork + d.B * d.Hkv, kThreads, 0, s>>>(p);
+  // with a workspace: + one workgroup per (b, kv head) for the dK/dV work order
+  const int extra = cmask ? d.B * d.Hkv : 0;
+  attend_bwd_dq_kernel<T, D, TK, S><<<p.nwork + extra, kThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t run_prep(const Dims& d, const void* O, const void* dO, const int32_t* gi,
+                    float* delta, uint8_t* cmask, int32_t* order, hipStream_t s) {
+  const DqP p = dq_params<T, D>(d, nullptr, nullptr, nullptr, O, nullptr, dO, gi, nullptr,
+                                delta, cmask, order);
+  attend_bwd_prep_kernel<T, D><<<p.nwork + d.B * d.Hkv, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -426,6 +505,16 @@ hipError_t launch_attend_bwd_dq(const Dims& d, const void* Q, const void* K, con
                       : run_dq<uint16_t, 64>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, order, s);
   return d.D == 128 ? run_dq<float, 128>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, order, s)
                     : run_dq<float, 64>(d, Q, K, V, O, lse, dO, group_idx, dQ, delta, cmask, order, s);
+}
+
+hipError_t launch_attend_bwd_prep(const Dims& d, const void* O, const void* dO,
+                                  const int32_t* group_idx, float* delta, uint8_t* cmask,
+                                  int32_t* order, hipStream_t s) {
+  if (d.bf16)
+    return d.D == 128 ? run_prep<uint16_t, 128>(d, O, dO, group_idx, delta, cmask, order, s)
+                      : run_prep<uint16_t, 64>(d, O, dO, group_idx, delta, cmask, order, s);
+  return d.D == 128 ? run_prep<float, 128>(d, O, dO, group_idx, delta, cmask, order, s)
+                    : run_prep<float, 64>(d, O, dO, group_idx, delta, cmask, order, s);
 }
 
 }  // namespace hga

@@ -201,9 +201,28 @@ hga_status hga_attend_bwd_dq(const hga_shape* shape, const void* Q, const void* 
   if (st != HGA_OK) return st;
   if (!Q || !K || !V || !O || !lse || !dO || !dQ) return HGA_ERR_NULL;
   if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
+  // no workspace: dQ only (the caller runs hga_attend_bwd_prep for dK/dV)
+  if (!workspace && workspace_bytes == 0)
+    return from_hip(hga::launch_attend_bwd_dq(dims_of(shape), Q, K, V, O, lse, dO, group_idx,
+                                              dQ, nullptr, nullptr, nullptr,
+                                              (hipStream_t)stream));
   if (!workspace || workspace_bytes < ::workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
   return from_hip(hga::launch_attend_bwd_dq(
       dims_of(shape), Q, K, V, O, lse, dO, group_idx, dQ, (float*)workspace,
+      (uint8_t*)workspace + delta_bytes(shape), order_full(shape, workspace),
+      (hipStream_t)stream));
+}
+
+hga_status hga_attend_bwd_prep(const hga_shape* shape, const void* O, const void* dO,
+                               const int32_t* group_idx, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!O || !dO) return HGA_ERR_NULL;
+  if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
+  if (!workspace || workspace_bytes < ::workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
+  return from_hip(hga::launch_attend_bwd_prep(
+      dims_of(shape), O, dO, group_idx, (float*)workspace,
       (uint8_t*)workspace + delta_bytes(shape), order_full(shape, workspace),
       (hipStream_t)stream));
 }

@@ -33,6 +33,12 @@ hipError_t launch_attend_bwd_dq(const Dims& d, const void* Q, const void* K, con
                                 const int32_t* group_idx, void* dQ, float* delta,
                                 uint8_t* cmask, int32_t* order, hipStream_t s);
 
+// delta, the group-mask map and the dK/dV work order (what the dQ kernel
+// writes into the workspace when given one), without dQ.
+hipError_t launch_attend_bwd_prep(const Dims& d, const void* O, const void* dO,
+                                  const int32_t* group_idx, float* delta, uint8_t* cmask,
+                                  int32_t* order, hipStream_t s);
+
 hipError_t launch_attend_bwd_dkdv(const Dims& d, const void* Q, const void* K, const void* V,
                                   const float* lse, const void* dO, const int32_t* group_idx,
                                   const float* delta, const uint8_t* cmask, int32_t* order,

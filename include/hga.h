@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 6
+#define HGA_ABI_VERSION 7
 #define HGA_CHUNK 64      /* tokens per chunk (the page's 64-token chunks) */
 #define HGA_GROUP 8       /* tokens per group (the page's 8-token groups)  */
 #define HGA_QBLOCK 64     /* queries per routing block                      */
@@ -227,9 +227,12 @@ hga_status hga_attend_bwd_noalloc(const hga_shape* shape, const void* Q, const v
  * whole chunk range into the workspace; hga_attend_bwd_dkdv then reads them
  * from the same workspace and computes dK and dV.  The dkdv call must follow
  * a dq call with the same inputs, on the same stream (or after it has
- * completed).  A dkdv call on a workspace that no such dq call wrote gives
- * unspecified dK/dV values but never writes outside dK and dV: work-order
- * entries outside the chunk range are skipped. */
+ * completed), or a hga_attend_bwd_prep call (below).  A dkdv call on a
+ * workspace that neither wrote gives unspecified dK/dV values but never
+ * writes outside dK and dV: work-order entries outside the chunk range are
+ * skipped.
+ * hga_attend_bwd_dq with workspace == NULL and workspace_bytes == 0 computes
+ * dQ only and touches no workspace. */
 hga_status hga_attend_bwd_dq(const hga_shape* shape, const void* Q, const void* K,
                              const void* V, const void* O, const float* lse, const void* dO,
                              const int32_t* group_idx, void* dQ, void* workspace,
@@ -238,6 +241,19 @@ hga_status hga_attend_bwd_dkdv(const hga_shape* shape, const void* Q, const void
                                const void* V, const float* lse, const void* dO,
                                const int32_t* group_idx, void* dK, void* dV,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* What hga_attend_bwd_dq writes into the workspace (delta, the group-mask map,
+ * the whole range's dK/dV work order), computed from O, dO and the routing
+ * alone, without dQ: after it, hga_attend_bwd_dkdv and a workspace-free
+ * hga_attend_bwd_dq depend on nothing but their inputs, so a caller may run
+ * them side by side on two streams (page section "What HGA does differently":
+ * the backward reaches Q, K and V as in dense attention; the two gradients
+ * are independent given the forward's outputs).  dK/dV after it are bitwise
+ * those after hga_attend_bwd_dq.
+ *   O, dO      [B][Hq][q_len][D] dtype; group_idx as for hga_attend_fwd */
+hga_status hga_attend_bwd_prep(const hga_shape* shape, const void* O, const void* dO,
+                               const int32_t* group_idx, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* hga_attend_bwd_dkdv restricted to the keys of chunks [chunk_begin,
  * chunk_end): only those rows of dK and dV are written (every row in the

@@ -178,6 +178,38 @@ def test_split_backward_matches_combined():
         assert torch.equal(x0, x1)
 
 
+def test_prep_then_side_by_side_backward_matches_combined():
+    """hga_attend_bwd_prep, then a workspace-free hga_attend_bwd_dq on a second
+    stream beside hga_attend_bwd_dkdv on the first (forked and joined by
+    events), give bit for bit what hga_attend_bwd gives; also in sequence."""
+    w = SMALL["bf16_seg_b2"]
+    x = syn.make_inputs(w, with_grad_output=True)
+    t = upload(x, "bf16")
+    s = shape_of(w)
+    o = hga.forward(s, t["Q"], t["K"], t["V"])
+    ws = torch.empty(hga.hga_attend_bwd_workspace(s), dtype=torch.uint8, device=DEV)
+    ref = [torch.empty_like(t["Q"]), torch.empty_like(t["K"]), torch.empty_like(t["V"])]
+    hga.hga_attend_bwd(s, t["Q"], t["K"], t["V"], o["O"], o["lse"], t["dO"], o["group_idx"],
+                       *ref, ws)
+    torch.cuda.synchronize()
+    for side_by_side in (False, True):
+        got = [torch.full_like(v, float("nan")) for v in ref]
+        ws.fill_(0xFF)
+        main = torch.cuda.current_stream()
+        hga.hga_attend_bwd_prep(s, o["O"], t["dO"], o["group_idx"], ws)
+        side = torch.cuda.Stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side if side_by_side else main):
+            hga.hga_attend_bwd_dq(s, t["Q"], t["K"], t["V"], o["O"], o["lse"], t["dO"],
+                                  o["group_idx"], got[0], None)
+        hga.hga_attend_bwd_dkdv(s, t["Q"], t["K"], t["V"], o["lse"], t["dO"], o["group_idx"],
+                                got[1], got[2], ws)
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dQ", "dK", "dV"), ref, got):
+            assert torch.equal(a, b), (name, side_by_side)
+
+
 def test_incremental_summaries_match_full_build():
     w = SMALL["bf16_seg_b2"]
     x = syn.make_inputs(w)
