@@ -836,35 +836,44 @@ def main():
     phase_rep["routing_total"] = {"kernel_us": round(rt, 2), "algorithmic_bytes": rb,
                                   "achieved_GBs": round(rb / (rt * 1e-6) / 1e9, 1),
                                   "frac": round(rb / (rt * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-    if os.path.exists(hga.GATHER_LIB_PATH) and not args.causal:
-        Og = torch.empty_like(O)
-        lg = torch.empty_like(lse)
-        gus = kernel_us(lambda: hga.hga_attend_fwd(s, t["Q"], t["K"], t["V"], gi, Og, lg,
-                                                    library=hga.GATHER_LIB_PATH))
-        kept = int((gi >= 0).sum().item())
-        nrows = gi.shape[0] * gi.shape[1] * gi.shape[2]
-        esz = 2 if w.dtype == "bf16" else 4
-        logical = (kept * 8 + nrows * 64) * w.head_dim * esz * 2
-        unique = 0
-        gnp = gi.cpu().numpy()
-        for b in range(w.batch):
-            for h in range(w.n_kv_heads):
-                r = w.n_q_heads // w.n_kv_heads
-                sel = gnp[b, h * r:(h + 1) * r]
-                own = (w.kv_len - w.q_len) // 8 + np.arange(8 * (w.q_len // 64))
-                unique += len(np.union1d(np.unique(sel[sel >= 0]), own)) * 8
-        unique *= w.head_dim * esz * 2
-        ach = logical / (gus * 1e-6) / 1e9
-        phase_rep["gather"] = {
-            "kernel_us": round(gus, 2), "bound": "hbm", "logical_bytes": logical,
-            "unique_bytes": unique, "achieved_GBs": round(ach, 1),
-            "frac_logical": round(ach / PEAK_HBM_GBS, 4),
-            "unique_GBs": round(unique / (gus * 1e-6) / 1e9, 1),
-            "traffic": load_traffic("gather"),
-            "note": "the forward kernel built without its products (same routing-row load, "
-                    "tile walk, direct loads, waits and barriers); logical bytes count every "
-                    "gathered K and V row each time it is gathered, most served from the "
-                    "GPU's caches, so the logical rate may exceed the HBM peak"}
+    # the gather: the K/V rows the forward and dQ kernels move into LDS (every
+    # kept group and the own chunk, per routing row) and the Q/dO rows the
+    # dK/dV kernel moves (per (routing row, chunk) it attends), over each
+    # kernel's whole time with its products: a lower bound on the rate the
+    # gather itself sustains.  Logical bytes count a row each time it is
+    # gathered; most are served from the GPU's caches, so the logical rate may
+    # exceed the HBM peak.  The HBM bytes the kernels move are the counter
+    # figures (`traffic`).
+    kept = int((gi >= 0).sum().item())
+    nrows = gi.shape[0] * gi.shape[1] * gi.shape[2]
+    esz = 2 if w.dtype == "bf16" else 4
+    gnp = gi.cpu().numpy()
+    kv_logical = (kept * 8 + nrows * 64) * w.head_dim * esz * 2
+    unique = 0
+    r = w.n_q_heads // w.n_kv_heads
+    own = (w.kv_len - w.q_len) // 8 + np.arange(8 * (w.q_len // 64))
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            sel = gnp[b, h * r:(h + 1) * r]
+            unique += len(np.union1d(np.unique(sel[sel >= 0]), own)) * 8
+    unique *= w.head_dim * esz * 2
+    gather = {"kv_rows_logical_bytes": kv_logical, "kv_rows_unique_bytes": unique}
+    kernels = ["attend_fwd"] + ([] if fwd_only else ["attend_bwd_dq", "attend_bwd_dkdv"])
+    for k in kernels:
+        if k == "attend_bwd_dkdv":
+            entries = 0
+            for row in gnp.reshape(-1, gnp.shape[-1]):
+                v = row[row >= 0]
+                entries += len(np.unique(v >> 3)) + 1
+            logical = entries * 64 * (2 * w.head_dim * esz + 8)
+        else:
+            logical = kv_logical
+        us = phase_rep[k]["kernel_us"]
+        ach = logical / (us * 1e-6) / 1e9
+        gather[k] = {"logical_bytes": logical, "kernel_us": us, "achieved_GBs": round(ach, 1),
+                     "frac_of_hbm_peak": round(ach / PEAK_HBM_GBS, 4),
+                     "hbm_traffic": load_traffic(k)}
+    phase_rep["gather"] = gather
 
     base = None
     if not args.no_cpu_baseline:

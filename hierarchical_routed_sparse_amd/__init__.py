@@ -68,9 +68,6 @@ def make_shape(batch, n_q_heads, n_kv_heads, head_dim, q_len, kv_len, top_k, top
 _libs = {}
 _vp = ctypes.c_void_p
 _SP = ctypes.POINTER(HgaShape)
-# the gather-only measurement build of the library (the forward kernel with its
-# products left out); only the benchmark's gather phase calls it
-GATHER_LIB_PATH = os.path.join(HERE, "libhga_gather.so")
 
 
 def lib_path() -> str:
@@ -272,11 +269,10 @@ def hga_route_causal(shape, Q, Q_prev, chunk_mean, group_mean, chunk_idx, group_
         _stream(stream)), "hga_route_causal")
 
 
-def hga_attend_fwd(shape, Q, K, V, group_idx, O, lse=None, stream=None, library=None):
-    """``library``: GATHER_LIB_PATH selects the gather-only measurement build."""
+def hga_attend_fwd(shape, Q, K, V, group_idx, O, lse=None, stream=None):
     import torch
     sz, dt = _sizes(shape), _elt_dtype(shape)
-    _check(_load(library).hga_attend_fwd(
+    _check(_load().hga_attend_fwd(
         ctypes.byref(shape), _ptr(Q, "Q", dt, sz["q"]), _ptr(K, "K", dt, sz["kv"], host_ok=True),
         _ptr(V, "V", dt, sz["kv"], host_ok=True),
         _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),

@@ -56,12 +56,6 @@ def _compile(src: str, extra, build_dir=BUILD, csrc=CSRC) -> str:
     return obj
 
 
-# The gather-only measurement library: the same sources, with the forward
-# kernel compiled without its products (HGA_GATHER_ONLY, see attend_fwd.hip);
-# only the benchmark's gather phase loads it.
-GATHER_LIB = os.path.join(HERE, "libhga_gather.so")
-
-
 def _link(objs, out):
     tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
@@ -72,29 +66,16 @@ def _link(objs, out):
 
 
 def build(verbose: bool = False, extra=(), out: str = LIB, build_dir: str = BUILD,
-          csrc: str = CSRC, gather: bool = True) -> str:
+          csrc: str = CSRC) -> str:
     """Compiles every HIP source and links libhga.so (or `out`); returns its path.
     `extra` holds additional hipcc flags, e.g. -D overrides of tuning constants;
-    `csrc` may point at another copy of the sources.  With `gather`, also
-    links the gather-only measurement library next to it."""
+    `csrc` may point at another copy of the sources."""
     os.makedirs(build_dir, exist_ok=True)
-    jobs = [(s, list(extra), build_dir) for s in SOURCES]
-    gdir = os.path.join(build_dir, "gather")
-    if gather:
-        os.makedirs(gdir, exist_ok=True)
-        jobs.append(("attend_fwd.hip", list(extra) + ["-DHGA_GATHER_ONLY=1"], gdir))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        objs = list(ex.map(lambda j: _compile(j[0], j[1], j[2], csrc), jobs))
-    _link(objs[:len(SOURCES)], out)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra), build_dir, csrc), SOURCES))
+    _link(objs, out)
     if verbose:
         print(f"built {out}")
-    if gather:
-        gobjs = [o if not o.endswith("attend_fwd.o") else objs[-1] for o in objs[:len(SOURCES)]]
-        gout = os.path.join(os.path.dirname(out), os.path.basename(GATHER_LIB)) \
-            if out != LIB else GATHER_LIB
-        _link(gobjs, gout)
-        if verbose:
-            print(f"built {gout}")
     return out
 
 

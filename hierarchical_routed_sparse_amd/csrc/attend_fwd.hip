@@ -29,13 +29,6 @@
 #ifndef HGA_FWD_STAGES
 #define HGA_FWD_STAGES 2    // tiles resident in LDS (STAGES - 1 in flight)
 #endif
-// HGA_GATHER_ONLY=1 builds a measurement variant of this kernel (its own
-// library, never the product): the same routing-row load, tile walk, direct
-// loads, waits and barriers, with the products and the softmax left out, so
-// that its time is the gather's alone.  It writes O = 0 and lse = 0.
-#ifndef HGA_GATHER_ONLY
-#define HGA_GATHER_ONLY 0
-#endif
 
 namespace hga {
 namespace {
@@ -186,7 +179,6 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
     else wait_vmcnt<0>();
     __syncthreads();   // tile ti visible to all; everyone is done with tile ti-1
     if (ti + S - 1 < ntiles) issue(ti + S - 1, gnext);
-    if constexpr (HGA_GATHER_ONLY != 0) continue;
 
     const char* kt = smem + (ti % S) * kStage;
     const char* vt = kt + kTileBytes;
@@ -287,10 +279,6 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
   }
 
   // epilogue: normalise, write O (4 consecutive elements per lane) and lse
-  if constexpr (HGA_GATHER_ONLY != 0) {
-    l_run = 0.25f;
-    m_run = 0.f;
-  }
   const float l_tot = xor_sum16_32(l_run);
   const float inv = 1.0f / l_tot;
   T* o = reinterpret_cast<T*>(p.O) + (qrow0 + qq) * D + 4 * g4;
