@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--host-kv", action="store_true",
                     help="with --segments or --decode: keep the keys and values in pinned "
                          "host memory")
+    ap.add_argument("--stage", action="store_true",
+                    help="with --segments: stage each segment's routed working set (the "
+                         "distinct kept history groups and the segment's rows) into HBM")
     ap.add_argument("--causal", action="store_true",
                     help="strictly causal routing (block j routed with the 64 queries before it)")
     ap.add_argument("--decode", action="store_true",
@@ -336,7 +339,7 @@ def segments_main(args):
     torch.cuda.set_device(0)
     t = {k: syn.to_torch(v, w.dtype, dev) for k, v in x.items()}
     run = SegmentRunner(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, L, S, w.top_k, w.top_g,
-                        dtype=w.dtype, device=dev, kv_on_host=args.host_kv)
+                        dtype=w.dtype, device=dev, kv_on_host=args.host_kv, stage=args.stage)
     run.k_history.copy_(t["K"].cpu() if args.host_kv else t["K"])
     run.v_history.copy_(t["V"].cpu() if args.host_kv else t["V"])
     nseg = L // S
@@ -374,11 +377,24 @@ def segments_main(args):
         rows = w.batch * w.n_q_heads * (S // 64)
         gather = (kept * 8 + rows * 64) * row_bytes * 2
         own = w.batch * w.n_kv_heads * S * row_bytes
+        if args.stage:
+            # staged: each distinct kept history group and the segment's rows
+            # cross from the history once (K and V), plus the summaries' read
+            import torch as _t
+            sg = run.stage_groups[i]
+            off = -(-(w.batch * w.n_kv_heads * sg * 4) // 256) * 256
+            cnt = run.stage_ws[off:off + 4 * w.batch * w.n_kv_heads].view(_t.int32)
+            union = int(cnt.sum().item())
+            seg[i]["union_groups"] = union
+            seg[i]["staged_bytes_from_history"] = (union * 8 * row_bytes + own) * 2 + own
+            seg[i]["history_GBs"] = round(seg[i]["staged_bytes_from_history"]
+                                          / (seg[i]["ms"] * 1e-3) / 1e9, 1)
         seg[i]["kv_bytes_read"] = 2 * gather + own + 2 * own
         seg[i]["kv_GBs"] = round(seg[i]["kv_bytes_read"] / (seg[i]["ms"] * 1e-3) / 1e9, 1)
     out = {
         "metric": "HGA segment-wise fwd+bwd query tokens/sec, 16K sequence as 8 x 2048 segments "
                   "(history detached" + (", K/V in pinned host memory" if args.host_kv else "")
+                  + (", routed working set staged in HBM per segment" if args.stage else "")
                   + "), 1 MI355X",
         "value": w.batch * L / (ms_pass * 1e-3),
         "unit": "query tokens/s",

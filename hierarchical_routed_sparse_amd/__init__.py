@@ -27,7 +27,7 @@ __all__ = [
     "hga_build_summaries", "hga_route", "hga_route_causal", "hga_attend_fwd", "hga_attend_bwd_workspace",
     "hga_attend_bwd", "hga_attend_bwd_noalloc", "hga_attend_bwd_prep", "hga_attend_bwd_dq", "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range",
     "hga_validate_decode_shape", "hga_decode", "hga_decode_route", "hga_decode_attend",
-    "hga_decode_route_causal",
+    "hga_decode_route_causal", "hga_stage_min_groups", "hga_stage_workspace", "hga_stage_routed",
     "forward", "backward", "decode",
 ]
 
@@ -103,12 +103,17 @@ def _load(path: str = None):
     lib.hga_decode_route.argtypes = [_SP] + [_vp] * 6
     lib.hga_decode_attend.argtypes = [_SP] + [_vp] * 7
     lib.hga_decode_route_causal.argtypes = [_SP] + [_vp] * 6
+    lib.hga_stage_min_groups.argtypes = [_SP]
+    lib.hga_stage_min_groups.restype = ctypes.c_int32
+    lib.hga_stage_workspace.argtypes = [_SP, i32, ctypes.POINTER(sz)]
+    lib.hga_stage_routed.argtypes = [_SP, _vp, _vp, _vp, i32, i32, _vp, _vp, _vp, _vp, sz, _vp]
     for name in ("hga_validate_shape", "hga_validate_decode_shape", "hga_decode", "hga_route_causal",
                  "hga_decode_route", "hga_decode_attend", "hga_decode_route_causal", "hga_build_summaries", "hga_route", "hga_attend_fwd",
                  "hga_attend_bwd_workspace", "hga_attend_bwd", "hga_attend_bwd_noalloc",
                  "hga_attend_bwd_prep",
                  "hga_attend_bwd_dq",
-                 "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range"):
+                 "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range", "hga_stage_workspace",
+                 "hga_stage_routed"):
         getattr(lib, name).restype = ctypes.c_int
     _libs[path] = lib
     return lib
@@ -430,6 +435,35 @@ def hga_decode_attend(shape, Q, K, V, group_idx, O, lse=None, stream=None):
         _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
         _ptr(O, "O", dt, sz["q"]), _ptr(lse, "lse", torch.float32, sz["lse"], nullable=True),
         _stream(stream)), "hga_decode_attend")
+
+
+def hga_stage_min_groups(shape) -> int:
+    return int(_load().hga_stage_min_groups(ctypes.byref(shape)))
+
+
+def hga_stage_workspace(shape, stage_groups) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_load().hga_stage_workspace(ctypes.byref(shape), int(stage_groups), ctypes.byref(n)),
+           "hga_stage_workspace")
+    return int(n.value)
+
+
+def hga_stage_routed(shape, group_idx, K, V, stage_groups, K_stage, V_stage, group_idx_staged,
+                     workspace, stream=None):
+    """Stages the routed working set (see include/hga.h); K_stage and V_stage
+    [B, Hkv, stage_capacity, D] device tensors."""
+    import torch
+    sz, dt = _sizes(shape), _elt_dtype(shape)
+    cap = K_stage.shape[2]
+    st = (shape.batch, shape.n_kv_heads, cap, shape.head_dim)
+    wp, wb = _ws(workspace)
+    _check(_load().hga_stage_routed(
+        ctypes.byref(shape), _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        _ptr(K, "K", dt, sz["kv"], host_ok=True), _ptr(V, "V", dt, sz["kv"], host_ok=True),
+        int(stage_groups), int(cap), _ptr(K_stage, "K_stage", dt, st),
+        _ptr(V_stage, "V_stage", dt, st),
+        _ptr(group_idx_staged, "group_idx_staged", torch.int32, sz["gi"], nullable=True),
+        wp, wb, _stream(stream)), "hga_stage_routed")
 
 
 # ------------------------------------------------------------------ compositions

@@ -274,6 +274,54 @@ hga_status hga_attend_bwd(const hga_shape* shape, const void* Q, const void* K, 
                              workspace_bytes, stream);
 }
 
+int32_t hga_stage_min_groups(const hga_shape* shape) {
+  if (hga_validate_shape(shape) != HGA_OK) return -1;
+  // the union of a kv head's kept history groups is at most every history
+  // group, and at most every row's top_g
+  const long long hist = 8LL * ((shape->kv_len - shape->q_len) / HGA_CHUNK);
+  const long long sel = (long long)(shape->n_q_heads / shape->n_kv_heads) *
+                        (shape->q_len / HGA_QBLOCK) * shape->top_g;
+  const long long need = hist < sel ? hist : sel;
+  return (int32_t)((need + 7) / 8 * 8);
+}
+
+hga_status hga_stage_workspace(const hga_shape* shape, int32_t stage_groups, size_t* bytes) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!bytes) return HGA_ERR_NULL;
+  if (stage_groups < 0 || stage_groups % 8 != 0) return HGA_ERR_SHAPE;
+  *bytes = round256((size_t)shape->batch * shape->n_kv_heads * (size_t)stage_groups *
+                    sizeof(int32_t)) +
+           round256((size_t)shape->batch * shape->n_kv_heads * sizeof(int32_t));
+  return HGA_OK;
+}
+
+hga_status hga_stage_routed(const hga_shape* shape, const int32_t* group_idx, const void* K,
+                            const void* V, int32_t stage_groups, int32_t stage_capacity,
+                            void* K_stage, void* V_stage, int32_t* group_idx_staged,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!K || !V || !K_stage || !V_stage) return HGA_ERR_NULL;
+  if (shape->top_g > 0 && (!group_idx || !group_idx_staged)) return HGA_ERR_NULL;
+  if (stage_groups % 8 != 0 || stage_groups < hga_stage_min_groups(shape)) return HGA_ERR_SHAPE;
+  if (stage_capacity % HGA_CHUNK != 0 || stage_capacity < 8 * stage_groups + shape->q_len ||
+      stage_capacity > HGA_MAX_KV_LEN)
+    return HGA_ERR_SHAPE;
+  size_t need = 0;
+  st = hga_stage_workspace(shape, stage_groups, &need);
+  if (st != HGA_OK) return st;
+  if (!workspace || workspace_bytes < need) return HGA_ERR_WORKSPACE;
+  int32_t* ulist = (int32_t*)workspace;
+  int32_t* ucount = (int32_t*)((uint8_t*)workspace +
+                               round256((size_t)shape->batch * shape->n_kv_heads *
+                                        (size_t)stage_groups * sizeof(int32_t)));
+  return from_hip(hga::launch_stage(dims_of(shape), shape->top_g > 0 ? group_idx : nullptr, K,
+                                    V, stage_groups, stage_capacity, K_stage, V_stage,
+                                    shape->top_g > 0 ? group_idx_staged : nullptr, ulist,
+                                    ucount, (hipStream_t)stream));
+}
+
 hga_status hga_decode_route(const hga_shape* shape, const void* Q, const float* chunk_mean,
                             const float* group_mean, int32_t* chunk_idx, int32_t* group_idx,
                             void* stream) {

@@ -45,6 +45,11 @@ hipError_t launch_attend_bwd_dkdv(const Dims& d, const void* Q, const void* K, c
                                   bool order_ready, void* dK, void* dV, int chunk_begin,
                                   int chunk_end, hipStream_t s);
 
+// The routed working set of a segment staged into a compact buffer (stage.hip).
+hipError_t launch_stage(const Dims& d, const int32_t* gidx, const void* K, const void* V,
+                        int sg, int scap_s, void* Ks, void* Vs, int32_t* gidx_out,
+                        int32_t* ulist, int32_t* ucount, hipStream_t s);
+
 // Decode attention (one query per (b, hq) at position Skv - 1; d.Sq == 1).
 hipError_t launch_decode_attend(const Dims& d, const void* Q, const void* K, const void* V,
                                 const int32_t* group_idx, void* O, float* lse, hipStream_t s);

@@ -34,6 +34,14 @@ With ``kv_on_host=True`` the key/value history lives in pinned host memory
 (the page's RAM tier, same section): the summaries stay in GPU memory, and the
 kernels fetch only the rows they gather (the kept groups, the own chunk, the
 segment's keys for its dK/dV) across the host link.
+
+With ``stage=True`` each segment's routed working set is staged into device
+memory once, after its routing (``hga_stage_routed``): the distinct history
+groups its rows kept and the segment's own rows go into a compact device
+buffer, the routing rows are rewritten against it, and the attention and
+backward run there.  Each kept row then crosses the host link once per
+segment, however many rows gather it; results equal the unstaged ones bit
+for bit.
 """
 from __future__ import annotations
 
@@ -41,7 +49,8 @@ import contextlib
 from dataclasses import dataclass
 
 from . import (CHUNK, hga_attend_bwd_dkdv_range, hga_attend_bwd_dq, hga_attend_bwd_workspace,
-               hga_attend_fwd, hga_build_summaries, hga_route, hga_route_causal, make_shape)
+               hga_attend_fwd, hga_build_summaries, hga_route, hga_route_causal,
+               hga_stage_min_groups, hga_stage_routed, hga_stage_workspace, make_shape)
 
 
 @dataclass
@@ -58,7 +67,7 @@ class SegmentRunner:
     def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int,
                  seg_len: int, top_k: int, top_g: int, dtype: str = "bf16",
                  softmax_scale: float = 0.0, device="cuda:0", kv_on_host: bool = False,
-                 causal: bool = False):
+                 causal: bool = False, stage: bool = False):
         import torch
         if seg_len % CHUNK or seq_len % seg_len:
             raise ValueError("seg_len must be a multiple of 64 dividing seq_len")
@@ -95,12 +104,40 @@ class SegmentRunner:
         # the last segment needs the largest workspace (longest history)
         self.workspace = torch.empty(hga_attend_bwd_workspace(self.shape(self.nseg - 1)),
                                      dtype=torch.uint8, device=device)
+        self.stage = stage
+        if stage:
+            # the staged history of the last segment is the largest the bound
+            # allows: every history group, or every row's top_g
+            sg_max = max(hga_stage_min_groups(self.shape(i)) for i in range(self.nseg))
+            self.stage_cap = -(-(8 * sg_max + seg_len) // 64) * 64
+            st = (batch, n_kv_heads, self.stage_cap, head_dim)
+            self.k_stage = torch.empty(st, dtype=elt, device=device)
+            self.v_stage = torch.empty(st, dtype=elt, device=device)
+            self.dk_stage = torch.empty(st, dtype=elt, device=device)
+            self.dv_stage = torch.empty(st, dtype=elt, device=device)
+            self.group_idx_staged = torch.empty_like(self.group_idx)
+            self.stage_ws = torch.empty(max(256, hga_stage_workspace(self.shape(self.nseg - 1),
+                                                                     sg_max)),
+                                        dtype=torch.uint8, device=device)
+            big = make_shape(batch, n_q_heads, n_kv_heads, head_dim, seg_len, self.stage_cap,
+                             top_k, top_g, dtype=dtype, softmax_scale=softmax_scale)
+            self.workspace = torch.empty(max(self.workspace.numel(),
+                                             hga_attend_bwd_workspace(big)),
+                                         dtype=torch.uint8, device=device)
+            self.stage_groups = [hga_stage_min_groups(self.shape(i)) for i in range(self.nseg)]
 
     def shape(self, i: int):
         """Shape of segment i: q_len = S at the end of kv_len = (i+1) S."""
         return make_shape(self.B, self.Hq, self.Hkv, self.D, self.S, (i + 1) * self.S,
                           self.top_k, self.top_g, dtype=self.dtype,
                           softmax_scale=self.scale, kv_capacity=self.L)
+
+    def staged_shape(self, i: int):
+        """Shape of segment i over its staged working set."""
+        return make_shape(self.B, self.Hq, self.Hkv, self.D, self.S,
+                          8 * self.stage_groups[i] + self.S, self.top_k, self.top_g,
+                          dtype=self.dtype, softmax_scale=self.scale,
+                          kv_capacity=self.stage_cap)
 
     def forward(self, i: int, Q, stream=None):
         """Steps 1-3 for segment i (its keys/values already in the history)."""
@@ -114,8 +151,15 @@ class SegmentRunner:
         else:
             hga_route(s, Q, self.chunk_mean, self.group_mean, self.chunk_idx, self.group_idx,
                       stream=stream)
-        hga_attend_fwd(s, Q, self.k_history, self.v_history, self.group_idx, self.O, self.lse,
-                       stream=stream)
+        if self.stage:
+            hga_stage_routed(s, self.group_idx, self.k_history, self.v_history,
+                             self.stage_groups[i], self.k_stage, self.v_stage,
+                             self.group_idx_staged, self.stage_ws, stream=stream)
+            hga_attend_fwd(self.staged_shape(i), Q, self.k_stage, self.v_stage,
+                           self.group_idx_staged, self.O, self.lse, stream=stream)
+        else:
+            hga_attend_fwd(s, Q, self.k_history, self.v_history, self.group_idx, self.O,
+                           self.lse, stream=stream)
         if self.causal:
             # the next segment's first block routes with this segment's last 64 queries
             import torch
@@ -125,6 +169,22 @@ class SegmentRunner:
     def backward(self, i: int, Q, dO, stream=None):
         """Step 4 for segment i, after forward(i, Q): dQ, and dK, dV of the
         segment's own keys (history detached)."""
+        if self.stage:
+            import torch
+            s = self.staged_shape(i)
+            c0 = self.stage_groups[i] // 8
+            c1 = c0 + self.S // CHUNK
+            hga_attend_bwd_dq(s, Q, self.k_stage, self.v_stage, self.O, self.lse, dO,
+                              self.group_idx_staged, self.dQ, self.workspace, stream=stream)
+            hga_attend_bwd_dkdv_range(s, Q, self.k_stage, self.v_stage, self.lse, dO,
+                                      self.group_idx_staged, c0, c1, self.dk_stage,
+                                      self.dv_stage, self.workspace, stream=stream)
+            rows = slice(i * self.S, (i + 1) * self.S)
+            srows = slice(64 * c0, 64 * c1)
+            with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
+                self.dK[:, :, rows].copy_(self.dk_stage[:, :, srows])
+                self.dV[:, :, rows].copy_(self.dv_stage[:, :, srows])
+            return
         s = self.shape(i)
         c0, c1 = i * self.S // CHUNK, (i + 1) * self.S // CHUNK
         hga_attend_bwd_dq(s, Q, self.k_history, self.v_history, self.O, self.lse, dO,

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 7
+#define HGA_ABI_VERSION 8
 #define HGA_CHUNK 64      /* tokens per chunk (the page's 64-token chunks) */
 #define HGA_GROUP 8       /* tokens per group (the page's 8-token groups)  */
 #define HGA_QBLOCK 64     /* queries per routing block                      */
@@ -269,6 +269,44 @@ hga_status hga_attend_bwd_dkdv_range(const hga_shape* shape, const void* Q, cons
                                      const int32_t* group_idx, int32_t chunk_begin,
                                      int32_t chunk_end, void* dK, void* dV, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/* The routed working set of a segment in device memory (page section "What
+ * HGA does differently", memory paragraph: GPU memory holds the summaries, the
+ * active segment and the routed working set, while older keys and values live
+ * in host RAM).  After routing a segment (q_len queries at the end of kv_len,
+ * its K and V typically pinned host memory), this call copies, per (b, kv
+ * head), the distinct history groups its rows kept (their union, ascending)
+ * and then the segment's own rows into a compact device buffer, and rewrites
+ * every routing row against it.  The attention and backward calls then take
+ * the staged shape: q_len as given, kv_len = 8 * stage_groups + q_len,
+ * kv_capacity = stage_capacity, with K_stage, V_stage and group_idx_staged;
+ * O, lse, dQ and the segment's dK/dV rows (chunks stage_groups / 8 onwards)
+ * equal those over the full history bit for bit.
+ *   group_idx         [B][Hq][q_len/64][top_g] as written by the routing
+ *                     (read by the prefix rule of hga_attend_fwd)
+ *   K, V              [B][Hkv][C][D] dtype, the full history (C =
+ *                     kv_capacity or kv_len)
+ *   stage_groups      group slots of the staged history, a multiple of 8 and
+ *                     at least hga_stage_min_groups(shape): the union always
+ *                     fits
+ *   stage_capacity    rows per (b, kv head) of K_stage and V_stage, a
+ *                     multiple of 64, >= 8 * stage_groups + q_len
+ *   K_stage, V_stage  [B][Hkv][stage_capacity][D] dtype, device memory:
+ *                     rows 8k..8k+7 = union group k; rows 8 * stage_groups ..
+ *                     + q_len - 1 = the segment; slots past the union are
+ *                     not written
+ *   group_idx_staged  [B][Hq][q_len/64][top_g] int32: a history group g ->
+ *                     its rank in the union, a group of the segment ->
+ *                     g - 8 (kv_len - q_len)/64 + stage_groups, -1 padded
+ *   workspace         hga_stage_workspace(shape, stage_groups) bytes: the
+ *                     unions ([B][Hkv][stage_groups] int32) and their sizes
+ *                     ([B][Hkv] int32) */
+int32_t hga_stage_min_groups(const hga_shape* shape);   /* -1 for an invalid shape */
+hga_status hga_stage_workspace(const hga_shape* shape, int32_t stage_groups, size_t* bytes);
+hga_status hga_stage_routed(const hga_shape* shape, const int32_t* group_idx, const void* K,
+                            const void* V, int32_t stage_groups, int32_t stage_capacity,
+                            void* K_stage, void* V_stage, int32_t* group_idx_staged,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Decode: attention of one new token per (b, query head) over a resident
  * key/value cache (page section "What HGA does differently", read for

@@ -58,3 +58,38 @@ def test_segments_with_host_kv_match_device():
     for a, b in zip(outs[0], outs[1]):
         for u, v in zip(a, b):
             assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("name,L,S,k,g,on_host", [
+    ("stage_dev", 1024, 256, 3, 12, False),
+    ("stage_host", 1024, 256, 3, 12, True),
+    # budgets that keep more groups than the history holds for early segments
+    # and fewer than it for late ones: the union bounded both ways
+    ("stage_host_wide", 2048, 256, 20, 150, True),
+])
+def test_staged_working_set_matches_unstaged(name, L, S, k, g, on_host):
+    """Segment-wise training with each segment's routed working set staged
+    into a compact device buffer gives, segment by segment, the unstaged
+    results bit for bit (O, lse, routing, dQ, the segment's dK and dV)."""
+    from gpu_common import DEV
+    print(f"[case] {name}", flush=True)
+    w = syn.Workload(name, 1, 4, 2, 128, L, L, k, g, "bf16", 43, 1 / math.sqrt(128),
+                     backward=True)
+    x = syn.make_inputs(w, with_grad_output=True)
+    t = {kk: syn.to_torch(v, "bf16", DEV) for kk, v in x.items()}
+    outs = []
+    for staged in (False, True):
+        run = SegmentRunner(1, 4, 2, 128, L, S, k, g, device=DEV,
+                            kv_on_host=on_host and staged, stage=staged)
+        run.k_history.copy_(t["K"].cpu() if (on_host and staged) else t["K"])
+        run.v_history.copy_(t["V"].cpu() if (on_host and staged) else t["V"])
+        seg = []
+        for i in range(L // S):
+            rows = slice(i * S, (i + 1) * S)
+            r = run.step(i, t["Q"][:, :, rows].contiguous(), t["dO"][:, :, rows].contiguous())
+            torch.cuda.synchronize()
+            seg.append([v.clone() for v in (r.O, r.lse, r.group_idx, r.dQ, r.dK, r.dV)])
+        outs.append(seg)
+    for i, (a, b) in enumerate(zip(outs[0], outs[1])):
+        for nm, u, v in zip(("O", "lse", "group_idx", "dQ", "dK", "dV"), a, b):
+            assert torch.equal(u, v), (i, nm)
