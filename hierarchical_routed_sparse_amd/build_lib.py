@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libhga.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["hga_api.hip", "summaries.hip", "route.hip", "attend_fwd.hip", "attend_bwd.hip",
-           "attend_bwd_dkdv.hip", "decode.hip", "noalloc.hip", "stage.hip"]
+           "attend_bwd_dkdv.hip", "decode.hip", "noalloc.hip", "stage.hip", "hga_validate.cpp"]
 HEADERS = ["hga_device.h", "hga_kernels.h", "bwd_common.h"]
 
 FLAGS = [

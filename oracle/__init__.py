@@ -19,28 +19,40 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hga_oracle.cpp")
-_LIB = os.path.join(_HERE, "liboracle_hga.so")
+# HGA_ORACLE_LIB selects another build of the same source (the tests' sanitizer
+# build); it is used as it is, never rebuilt here
+_LIB_ENV = os.environ.get("HGA_ORACLE_LIB")
+_LIB = _LIB_ENV or os.path.join(_HERE, "liboracle_hga.so")
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
 
 _dp = ctypes.POINTER(ctypes.c_double)
 _ip = ctypes.POINTER(ctypes.c_int32)
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compiles the oracle with g++ (no fast-math, no FP contraction)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        cmd = ["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-ffp-contract=off",
+def build(force: bool = True, out: str | None = None, sanitize: bool = False) -> str:
+    """Compiles the oracle with g++ (no fast-math, no FP contraction); with
+    `sanitize`, an address- and undefined-behaviour-sanitized build (to be
+    loaded with those runtimes preloaded) into `out`."""
+    lib = out or _LIB
+    if _LIB_ENV and out is None:
+        return lib
+    if force or not os.path.exists(lib):
+        tmp = lib + ".tmp"
+        opt = SANITIZE_FLAGS if sanitize else ["-O2"]
+        cmd = ["g++", *opt, "-std=c++17", "-shared", "-fPIC", "-ffp-contract=off",
                "-fno-fast-math", _SRC, "-o", tmp]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not _LIB_ENV and (not os.path.exists(_LIB) or
+                             os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         i = ctypes.c_int
