@@ -165,9 +165,10 @@ KERNEL_NAMES = {
 }
 
 
-def load_traffic(phase: str):
-    """HBM bytes per call of `phase`, summed over the kernels the call launches,
-    from the stored counter runs; None when any of them is missing or its
+def load_traffic(phase: str, workload: str):
+    """HBM bytes per call of `phase` at `workload`, summed over the kernels the
+    call launches, from the stored counter runs (profiles/hbm_traffic.json,
+    keyed by workload, then phase); None when any of them is missing or its
     sources changed since."""
     try:
         with open(PROFILE_TRAFFIC) as f:
@@ -176,7 +177,7 @@ def load_traffic(phase: str):
         return None
     total = 0.0
     for k in PHASE_KERNELS.get(phase, [phase]):
-        r = rec.get("kernels", {}).get(k)
+        r = rec.get("workloads", {}).get(workload, {}).get(k)
         if not r or r.get("source_sha") != source_hash(k):
             return None
         total += r.get("hbm_bytes_per_launch")
@@ -648,7 +649,7 @@ def decode_main(args):
     us = rep[dom]["kernel_us"]
     ach = work[dom] / (us * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": ach / PEAK_HBM_GBS, "traffic": None if args.host_kv else load_traffic(dom),
+            "frac": ach / PEAK_HBM_GBS, "traffic": None if args.host_kv else load_traffic(dom, w.name),
             "kernel": dom, "kernel_us": us, "algorithmic_per_launch": work[dom]}
     base = None
     if not args.no_cpu_baseline:
@@ -837,7 +838,7 @@ def main():
         roof = {"bound": "mfma", "achieved": amount / sec / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = load_traffic(dom)
+    roof["traffic"] = load_traffic(dom, w.name)
     roof["kernel"] = dom
     roof["launches"] = " + ".join(KERNEL_NAMES[k] for k in PHASE_KERNELS.get(dom, [dom]))
     roof["kernel_us"] = dom_us
@@ -888,7 +889,7 @@ def main():
         ach = logical / (us * 1e-6) / 1e9
         gather[k] = {"logical_bytes": logical, "kernel_us": us, "achieved_GBs": round(ach, 1),
                      "frac_of_hbm_peak": round(ach / PEAK_HBM_GBS, 4),
-                     "hbm_traffic": load_traffic(k)}
+                     "hbm_traffic": load_traffic(k, w.name)}
     phase_rep["gather"] = gather
 
     base = None
