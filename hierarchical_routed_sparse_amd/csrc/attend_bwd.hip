@@ -399,11 +399,23 @@ void attend_bwd_dq_kernel(const DqP p) {
     __syncthreads();
     write_cmask_row(p, row, nvalid, s_glist, reinterpret_cast<uint8_t*>(smem));
   }
-  T* dq = reinterpret_cast<T*>(p.dQ) + (qrow0 + qq) * D + 4 * g4;
   const float sc = p.scale;
+  if constexpr (sizeof(T) == 2) {
+    // the block's 64 dQ rows are contiguous: whole rows through the idle
+    // stage buffers, past the map row's scratch at the start of smem
+    constexpr int kOut = S * kStage - 64 * 2 * D;
+    static_assert(kOut >= 2048, "dQ staging clear of the map row scratch");
+    __syncthreads();   // every wave is done with the stage buffers
+    out_rows_put<D>(smem + kOut, dqacc, sc, qq, g4);
+    __syncthreads();
+    out_rows_flush<D>(smem + kOut, reinterpret_cast<char*>(p.dQ) + qrow0 * 2 * D, tid);
+  } else {
+    T* dq = reinterpret_cast<T*>(p.dQ) + (qrow0 + qq) * D + 4 * g4;
 #pragma unroll
-  for (int dd = 0; dd < D / 16; ++dd)
-    store4(dq + 16 * dd, dqacc[dd][0] * sc, dqacc[dd][1] * sc, dqacc[dd][2] * sc, dqacc[dd][3] * sc);
+    for (int dd = 0; dd < D / 16; ++dd)
+      store4(dq + 16 * dd, dqacc[dd][0] * sc, dqacc[dd][1] * sc, dqacc[dd][2] * sc,
+             dqacc[dd][3] * sc);
+  }
 }
 
 // The backward's preparation pass, for callers that run dQ and dK/dV side by

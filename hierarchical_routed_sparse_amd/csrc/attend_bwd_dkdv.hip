@@ -156,17 +156,6 @@ __global__ __launch_bounds__(kOrderThreads) void dkdv_order_kernel(const DkvP p,
   }
 }
 
-// XOR swizzle (in 16-byte units) of the bf16 dK/dV staging rows.  Writes: a
-// half-wave writes 8 bytes per lane, units 2dd + g/2 of 16 consecutive keys;
-// reads: 16 lanes read the 16 units of one row (D = 128: one row of 256 bytes,
-// 8 lanes and two rows of 128 bytes at D = 64).  Rows 2m and 2m + 1 share a
-// swizzle at D = 128 in bits 2-3, so the 16-lane passes of a ds_read_b128,
-// which mix the units of two neighbouring lane groups, stay conflict-free.
-template <int D>
-__device__ __forceinline__ int out_swz(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-
 template <typename T, int D, int S>
 __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p) {
   using RT = RowTile<T, D>;
@@ -436,43 +425,18 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
   // every key of the chunk is written (zero when nothing attends it)
   const float sc = p.scale;
   if constexpr (sizeof(T) == 2) {
-    // bf16: the chunk's dK and dV rows are one contiguous block each.  A lane
-    // holds 4 consecutive elements of one key per accumulator, so stored
-    // directly every instruction would write 32-byte pieces of 16 rows; the
-    // rows go through the (now idle) stage buffers instead and leave as whole
-    // rows, 16 bytes per lane.  Same bf16 values (rounded once, to nearest
-    // even), so the results are unchanged.
+    // bf16: the chunk's dK and dV rows are one contiguous block each; they
+    // leave as whole rows through the idle stage buffers
     static_assert(2 * 64 * D * 2 <= S * kStage, "dK/dV staging fits the stage buffers");
-    constexpr int OB = 2 * D;                       // bytes per output row
-    constexpr int kRounds = 64 * OB / (16 * kThreads);
     char* const sk = smem;
-    char* const sv = smem + 64 * OB;
+    char* const sv = smem + 64 * 2 * D;
     __syncthreads();   // every wave is done with the stage buffers
-#pragma unroll
-    for (int dd = 0; dd < D / 16; ++dd) {
-      const uint32_t off = (uint32_t)(kin * OB) +
-                           ((uint32_t)((2 * dd + (g4 >> 1)) ^ out_swz<D>(kin)) << 4) +
-                           ((uint32_t)(g4 & 1) << 3);
-      uint2 xk, xv;
-      xk.x = pack_bf16(dkacc[dd][0] * sc, dkacc[dd][1] * sc);
-      xk.y = pack_bf16(dkacc[dd][2] * sc, dkacc[dd][3] * sc);
-      xv.x = pack_bf16(dvacc[dd][0], dvacc[dd][1]);
-      xv.y = pack_bf16(dvacc[dd][2], dvacc[dd][3]);
-      *reinterpret_cast<uint2*>(sk + off) = xk;
-      *reinterpret_cast<uint2*>(sv + off) = xv;
-    }
+    out_rows_put<D>(sk, dkacc, sc, kin, g4);
+    out_rows_put<D>(sv, dvacc, 1.0f, kin, g4);
     __syncthreads();
     const long long crow = (long long)bh * p.Scap + (long long)c * kChunk;
-    char* const gk = reinterpret_cast<char*>(p.dK) + crow * OB;
-    char* const gv = reinterpret_cast<char*>(p.dV) + crow * OB;
-#pragma unroll
-    for (int j = 0; j < kRounds; ++j) {
-      const int o = 16 * (tid + kThreads * j);
-      const int row = o / OB, u = (o % OB) >> 4;
-      const uint32_t loff = (uint32_t)(row * OB) + ((uint32_t)(u ^ out_swz<D>(row)) << 4);
-      *reinterpret_cast<uint4*>(gk + o) = *reinterpret_cast<const uint4*>(sk + loff);
-      *reinterpret_cast<uint4*>(gv + o) = *reinterpret_cast<const uint4*>(sv + loff);
-    }
+    out_rows_flush<D>(sk, reinterpret_cast<char*>(p.dK) + crow * 2 * D, tid);
+    out_rows_flush<D>(sv, reinterpret_cast<char*>(p.dV) + crow * 2 * D, tid);
   } else {
     const long long krow = (long long)bh * p.Scap + (long long)c * kChunk + kin;
     T* dk = reinterpret_cast<T*>(p.dK) + krow * D + 4 * g4;

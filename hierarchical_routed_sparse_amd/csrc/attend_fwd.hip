@@ -281,10 +281,21 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(const FwdP p) {
   // epilogue: normalise, write O (4 consecutive elements per lane) and lse
   const float l_tot = xor_sum16_32(l_run);
   const float inv = 1.0f / l_tot;
-  T* o = reinterpret_cast<T*>(p.O) + (qrow0 + qq) * D + 4 * g4;
+  if constexpr (sizeof(T) == 2) {
+    // the block's 64 output rows are contiguous: whole rows through the idle
+    // stage buffers
+    static_assert(64 * 2 * D <= S * kStage, "O staging fits the stage buffers");
+    __syncthreads();   // every wave is done with the stage buffers
+    out_rows_put<D>(smem, oacc, inv, qq, g4);
+    __syncthreads();
+    out_rows_flush<D>(smem, reinterpret_cast<char*>(p.O) + qrow0 * 2 * D, tid);
+  } else {
+    T* o = reinterpret_cast<T*>(p.O) + (qrow0 + qq) * D + 4 * g4;
 #pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds)
-    store4(o + 16 * ds, oacc[ds][0] * inv, oacc[ds][1] * inv, oacc[ds][2] * inv, oacc[ds][3] * inv);
+    for (int ds = 0; ds < D / 16; ++ds)
+      store4(o + 16 * ds, oacc[ds][0] * inv, oacc[ds][1] * inv, oacc[ds][2] * inv,
+             oacc[ds][3] * inv);
+  }
   if (p.lse && g4 == 0) p.lse[qrow0 + qq] = (m_run + __log2f(l_tot)) * kLn2;
 }
 

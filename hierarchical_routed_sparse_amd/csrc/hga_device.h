@@ -199,6 +199,52 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
+// ----------------------------------------------------------------- output rows through LDS
+//
+// The attention kernels end with a 64-row bf16 output block (O, dQ, dK, dV)
+// that is one contiguous run in memory, held as MFMA results: lane (l16, g)
+// of the wave owning rows 16w..16w+15 holds elements 16dd + 4g .. + 3 of row
+// 16w + l16.  Stored directly, every instruction writes 32-byte pieces of 16
+// rows.  out_rows_put packs them (bf16, nearest even, as store4 does) into an
+// idle LDS area; after a barrier out_rows_flush writes the block as whole
+// rows, 16 bytes per lane.  Same values as the direct stores.
+//
+// XOR swizzle in 16-byte units: a half-wave writes 8 bytes per lane to units
+// 2dd + g/2 of 16 consecutive rows, and 16 lanes read the units of one row
+// (D = 128: 256-byte rows; D = 64: two 128-byte rows per 16 lanes).  Rows 2m
+// and 2m + 1 agree in the swizzle's bits 2-3 at D = 128, so the 16-lane passes
+// of a ds_read_b128, which mix the units of neighbouring lane groups, stay
+// conflict-free too.
+template <int D>
+__device__ __forceinline__ int out_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ void out_rows_put(char* lds, const f32x4 (&acc)[D / 16], float sc,
+                                             int row, int g4) {
+#pragma unroll
+  for (int dd = 0; dd < D / 16; ++dd) {
+    const uint32_t off = (uint32_t)(row * 2 * D) +
+                         ((uint32_t)((2 * dd + (g4 >> 1)) ^ out_swz<D>(row)) << 4) +
+                         ((uint32_t)(g4 & 1) << 3);
+    uint2 x;
+    x.x = pack_bf16(acc[dd][0] * sc, acc[dd][1] * sc);
+    x.y = pack_bf16(acc[dd][2] * sc, acc[dd][3] * sc);
+    *reinterpret_cast<uint2*>(lds + off) = x;
+  }
+}
+template <int D>
+__device__ __forceinline__ void out_rows_flush(const char* lds, char* out, int tid) {
+  constexpr int OB = 2 * D;
+#pragma unroll
+  for (int j = 0; j < 64 * OB / (16 * kThreads); ++j) {
+    const int o = 16 * (tid + kThreads * j);
+    const int row = o / OB, u = (o % OB) >> 4;
+    const uint32_t loff = (uint32_t)(row * OB) + ((uint32_t)(u ^ out_swz<D>(row)) << 4);
+    *reinterpret_cast<uint4*>(out + o) = *reinterpret_cast<const uint4*>(lds + loff);
+  }
+}
+
 // ----------------------------------------------------------------- tile staging
 //
 // A "pair" is a 4-row x 8-element block: rows 4q..4q+3 of a 64-row tile,
