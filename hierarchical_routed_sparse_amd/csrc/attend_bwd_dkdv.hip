@@ -435,8 +435,10 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
     out_rows_put<D>(sv, dvacc, 1.0f, kin, g4);
     __syncthreads();
     const long long crow = (long long)bh * p.Scap + (long long)c * kChunk;
-    out_rows_flush<D>(sk, reinterpret_cast<char*>(p.dK) + crow * 2 * D, tid);
-    out_rows_flush<D>(sv, reinterpret_cast<char*>(p.dV) + crow * 2 * D, tid);
+    // non-temporal: the Q and dO rows that other workgroups still gather keep
+    // their place in L2 (no later kernel of the step reads dK, dV)
+    out_rows_flush<D, true>(sk, reinterpret_cast<char*>(p.dK) + crow * 2 * D, tid);
+    out_rows_flush<D, true>(sv, reinterpret_cast<char*>(p.dV) + crow * 2 * D, tid);
   } else {
     const long long krow = (long long)bh * p.Scap + (long long)c * kChunk + kin;
     T* dk = reinterpret_cast<T*>(p.dK) + krow * D + 4 * g4;

@@ -233,15 +233,22 @@ __device__ __forceinline__ void out_rows_put(char* lds, const f32x4 (&acc)[D / 1
     *reinterpret_cast<uint2*>(lds + off) = x;
   }
 }
-template <int D>
+// NT: non-temporal stores, for outputs no later kernel of the step reads, so
+// that they do not displace rows the running kernel still gathers from L2.
+template <int D, bool NT = false>
 __device__ __forceinline__ void out_rows_flush(const char* lds, char* out, int tid) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   constexpr int OB = 2 * D;
 #pragma unroll
   for (int j = 0; j < 64 * OB / (16 * kThreads); ++j) {
     const int o = 16 * (tid + kThreads * j);
     const int row = o / OB, u = (o % OB) >> 4;
     const uint32_t loff = (uint32_t)(row * OB) + ((uint32_t)(u ^ out_swz<D>(row)) << 4);
-    *reinterpret_cast<uint4*>(out + o) = *reinterpret_cast<const uint4*>(lds + loff);
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(lds + loff);
+    if constexpr (NT)
+      __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(out + o));
+    else
+      *reinterpret_cast<u32x4_t*>(out + o) = x;
   }
 }
 
