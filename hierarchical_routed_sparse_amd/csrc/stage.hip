@@ -140,41 +140,55 @@ __global__ __launch_bounds__(kUnionThreads) void stage_union_kernel(const StageP
 }
 
 // Copies the staged rows: workgroup j < sg / 8 takes union slots 8j .. 8j+7
-// (64 token rows), the later ones 64 rows of the segment each.  A thread
-// moves a quarter of one row of K and of V, 16 bytes at a time.
+// (64 token rows), the later ones 64 rows of the segment each.  The 64 rows
+// are moved as one run of 64 * row_bytes destination bytes, 16 bytes per lane
+// and consecutive lanes on consecutive bytes, so a wave's load covers whole
+// rows (1 KB of K or V, from at most two source groups of 8 contiguous rows):
+// over the host link that is a few long reads rather than many 16-byte ones.
+// Every load of a thread is issued before its first store.
 __global__ __launch_bounds__(256) void stage_copy_kernel(const StageP p) {
   const int per_bh = p.sg / 8 + p.Sq / kChunk;
   const int bh = blockIdx.x / per_bh, j = blockIdx.x % per_bh;
-  const int tid = threadIdx.x, row = tid >> 2, quarter = tid & 3;
-  long long src_tok, dst_tok;
-  if (j < p.sg / 8) {
-    const int slot = 8 * j + row / 8;
-    if (slot >= p.ucount[bh]) return;
-    src_tok = (long long)p.ulist[(long long)bh * p.sg + slot] * 8 + row % 8;
-    dst_tok = (long long)slot * 8 + row % 8;
-  } else {
-    const int t = (j - p.sg / 8) * kChunk + row;
-    src_tok = (long long)p.q0 + t;
-    dst_tok = (long long)p.sg * 8 + t;
-  }
-  const int qb = p.row_bytes / 4;   // bytes per thread
-  const char* ks = reinterpret_cast<const char*>(p.K) + ((long long)bh * p.Scap + src_tok) * p.row_bytes + quarter * qb;
-  const char* vs = reinterpret_cast<const char*>(p.V) + ((long long)bh * p.Scap + src_tok) * p.row_bytes + quarter * qb;
-  char* kd = reinterpret_cast<char*>(p.Ks) + ((long long)bh * p.Scap_s + dst_tok) * p.row_bytes + quarter * qb;
-  char* vd = reinterpret_cast<char*>(p.Vs) + ((long long)bh * p.Scap_s + dst_tok) * p.row_bytes + quarter * qb;
+  const int tid = threadIdx.x;
+  const bool uni = j < p.sg / 8;
+  const int nslot = uni ? p.ucount[bh] - 8 * j : 8;   // groups of this workgroup present
+  const long long kvbase = (long long)bh * p.Scap, sbase = (long long)bh * p.Scap_s;
+  const int n = p.row_bytes / 64;   // 16-byte pieces per thread: 2, 4 or 8
   uint4 a[8], c[8];
-  const int n = qb / 16;   // 2 .. 8
+  long long dst[8];
+  bool ok[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 8; ++i) {
+    ok[i] = false;
+    dst[i] = 0;
     if (i < n) {
-      a[i] = reinterpret_cast<const uint4*>(ks)[i];
-      c[i] = reinterpret_cast<const uint4*>(vs)[i];
+      const int o = 16 * (tid + 256 * i);            // byte in the 64-row run
+      const int row = o / p.row_bytes, inrow = o % p.row_bytes;
+      long long src_tok, dst_tok;
+      if (uni) {
+        const int slot = 8 * j + row / 8;
+        ok[i] = row / 8 < nslot;
+        src_tok = ok[i] ? (long long)p.ulist[(long long)bh * p.sg + slot] * 8 + row % 8 : 0;
+        dst_tok = (long long)slot * 8 + row % 8;
+      } else {
+        const int t = (j - p.sg / 8) * kChunk + row;
+        ok[i] = true;
+        src_tok = (long long)p.q0 + t;
+        dst_tok = (long long)p.sg * 8 + t;
+      }
+      const long long src = (kvbase + src_tok) * p.row_bytes + inrow;
+      dst[i] = (sbase + dst_tok) * p.row_bytes + inrow;
+      if (ok[i]) {
+        a[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.K) + src);
+        c[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.V) + src);
+      }
     }
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    if (i < n) {
-      reinterpret_cast<uint4*>(kd)[i] = a[i];
-      reinterpret_cast<uint4*>(vd)[i] = c[i];
+    if (i < n && ok[i]) {
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(p.Ks) + dst[i]) = a[i];
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(p.Vs) + dst[i]) = c[i];
     }
 }
 
