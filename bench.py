@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--stage", action="store_true",
                     help="with --segments: stage each segment's routed working set (the "
                          "distinct kept history groups and the segment's rows) into HBM")
+    ap.add_argument("--seg-on-device", action="store_true",
+                    help="with --segments --stage: each segment's keys and values are also "
+                         "given in device memory (the active segment), and staged from there")
     ap.add_argument("--causal", action="store_true",
                     help="strictly causal routing (block j routed with the 64 queries before it)")
     ap.add_argument("--decode", action="store_true",
@@ -347,10 +350,18 @@ def segments_main(args):
     dOs = [t["dO"][:, :, i * S:(i + 1) * S].contiguous() for i in range(nseg)]
     stream = torch.cuda.current_stream()
 
+    # --seg-on-device: each segment's keys and values also in device memory, as
+    # a projection produces them (the active segment in VRAM); the staging then
+    # takes the segment's rows from there
+    Ks = Vs = [None] * nseg
+    if args.seg_on_device:
+        Ks = [t["K"][:, :, i * S:(i + 1) * S].contiguous() for i in range(nseg)]
+        Vs = [t["V"][:, :, i * S:(i + 1) * S].contiguous() for i in range(nseg)]
+
     def one_pass(ev=None):
         for i in range(nseg):
             if ev: ev[i][0].record(stream)
-            run.step(i, Qs[i], dOs[i], stream=stream)
+            run.step(i, Qs[i], dOs[i], stream=stream, K_seg=Ks[i], V_seg=Vs[i])
             if ev: ev[i][1].record(stream)
 
     for _ in range(args.warmup):
@@ -372,21 +383,30 @@ def segments_main(args):
     # dK/dV read the segment's own keys (and values)
     row_bytes = w.head_dim * 2
     for i in range(nseg):
-        run.forward(i, Qs[i], stream=stream)
+        run.forward(i, Qs[i], stream=stream, K_seg=Ks[i], V_seg=Vs[i])
         kept = int((run.group_idx >= 0).sum().item())
         rows = w.batch * w.n_q_heads * (S // 64)
         gather = (kept * 8 + rows * 64) * row_bytes * 2
         own = w.batch * w.n_kv_heads * S * row_bytes
         if args.stage:
-            # staged: each distinct kept history group and the segment's rows
-            # cross from the history once (K and V), plus the summaries' read
+            # staged: the distinct kept history groups and the segment's rows
+            # (K and V); a group the previous segment's staging held is copied
+            # from there in device memory, the rest from the history, which
+            # the summaries read too (the segment's keys)
             import torch as _t
             sg = run.stage_groups[i]
-            off = -(-(w.batch * w.n_kv_heads * sg * 4) // 256) * 256
-            cnt = run.stage_ws[off:off + 4 * w.batch * w.n_kv_heads].view(_t.int32)
+            nbh = w.batch * w.n_kv_heads
+            lb = -(-(nbh * sg * 4) // 256) * 256
+            ws = run.stage_wss[i % 2]
+            cnt = ws[lb:lb + 4 * nbh].view(_t.int32).cpu()
+            src = ws[lb + (-(-(4 * nbh) // 256) * 256):][:4 * nbh * sg].view(_t.int32).cpu()
+            src = src.view(nbh, sg)
             union = int(cnt.sum().item())
+            from_hist = sum(int((src[k, :int(cnt[k])] < 0).sum().item()) for k in range(nbh))
             seg[i]["union_groups"] = union
-            seg[i]["staged_bytes_from_history"] = (union * 8 * row_bytes + own) * 2 + own
+            seg[i]["union_groups_from_history"] = from_hist
+            seg[i]["staged_bytes_from_history"] = \
+                (from_hist * 8 * row_bytes + (0 if args.seg_on_device else own)) * 2 + own
             seg[i]["history_GBs"] = round(seg[i]["staged_bytes_from_history"]
                                           / (seg[i]["ms"] * 1e-3) / 1e9, 1)
         seg[i]["kv_bytes_read"] = 2 * gather + own + 2 * own
@@ -395,6 +415,7 @@ def segments_main(args):
         "metric": "HGA segment-wise fwd+bwd query tokens/sec, 16K sequence as 8 x 2048 segments "
                   "(history detached" + (", K/V in pinned host memory" if args.host_kv else "")
                   + (", routed working set staged in HBM per segment" if args.stage else "")
+                  + (", active segment in HBM" if args.seg_on_device else "")
                   + "), 1 MI355X",
         "value": w.batch * L / (ms_pass * 1e-3),
         "unit": "query tokens/s",

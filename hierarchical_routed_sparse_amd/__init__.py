@@ -28,7 +28,7 @@ __all__ = [
     "hga_attend_bwd", "hga_attend_bwd_noalloc", "hga_attend_bwd_prep", "hga_attend_bwd_dq", "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range",
     "hga_validate_decode_shape", "hga_decode", "hga_decode_route", "hga_decode_attend",
     "hga_decode_route_causal", "hga_stage_min_groups", "hga_stage_workspace", "hga_stage_routed",
-    "forward", "backward", "decode",
+    "HgaStagePrev", "hga_stage_routed_from", "forward", "backward", "decode",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,6 +70,14 @@ _vp = ctypes.c_void_p
 _SP = ctypes.POINTER(HgaShape)
 
 
+class HgaStagePrev(ctypes.Structure):
+    """hga_stage_prev of include/hga.h: the previous staging of the same history."""
+    _fields_ = [("K_stage", ctypes.c_void_p), ("V_stage", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("stage_groups", ctypes.c_int32),
+                ("stage_capacity", ctypes.c_int32), ("q0", ctypes.c_int32),
+                ("q_len", ctypes.c_int32)]
+
+
 def lib_path() -> str:
     return LIB_PATH
 
@@ -107,13 +115,16 @@ def _load(path: str = None):
     lib.hga_stage_min_groups.restype = ctypes.c_int32
     lib.hga_stage_workspace.argtypes = [_SP, i32, ctypes.POINTER(sz)]
     lib.hga_stage_routed.argtypes = [_SP, _vp, _vp, _vp, i32, i32, _vp, _vp, _vp, _vp, sz, _vp]
+    lib.hga_stage_routed_from.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp,
+                                          ctypes.POINTER(HgaStagePrev), i32, i32, _vp, _vp, _vp,
+                                          _vp, sz, _vp]
     for name in ("hga_validate_shape", "hga_validate_decode_shape", "hga_decode", "hga_route_causal",
                  "hga_decode_route", "hga_decode_attend", "hga_decode_route_causal", "hga_build_summaries", "hga_route", "hga_attend_fwd",
                  "hga_attend_bwd_workspace", "hga_attend_bwd", "hga_attend_bwd_noalloc",
                  "hga_attend_bwd_prep",
                  "hga_attend_bwd_dq",
                  "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range", "hga_stage_workspace",
-                 "hga_stage_routed"):
+                 "hga_stage_routed", "hga_stage_routed_from"):
         getattr(lib, name).restype = ctypes.c_int
     _libs[path] = lib
     return lib
@@ -464,6 +475,38 @@ def hga_stage_routed(shape, group_idx, K, V, stage_groups, K_stage, V_stage, gro
         _ptr(V_stage, "V_stage", dt, st),
         _ptr(group_idx_staged, "group_idx_staged", torch.int32, sz["gi"], nullable=True),
         wp, wb, _stream(stream)), "hga_stage_routed")
+
+
+def hga_stage_routed_from(shape, group_idx, K, V, stage_groups, K_stage, V_stage,
+                          group_idx_staged, workspace, K_seg=None, V_seg=None, prev=None,
+                          stream=None):
+    """hga_stage_routed with the previous staging and the segment's rows in
+    device memory as copy sources (see include/hga.h).  ``prev`` is None or a
+    dict with the previous call's K_stage, V_stage, workspace (tensors),
+    stage_groups, q0 and q_len; K_seg and V_seg [B, Hkv, q_len, D] device
+    tensors or None."""
+    import torch
+    sz, dt = _sizes(shape), _elt_dtype(shape)
+    cap = K_stage.shape[2]
+    st = (shape.batch, shape.n_kv_heads, cap, shape.head_dim)
+    seg = (shape.batch, shape.n_kv_heads, shape.q_len, shape.head_dim)
+    wp, wb = _ws(workspace)
+    pp = None
+    if prev is not None:
+        pcap = prev["K_stage"].shape[2]
+        pst = (shape.batch, shape.n_kv_heads, pcap, shape.head_dim)
+        pw, _ = _ws(prev["workspace"])
+        pp = ctypes.byref(HgaStagePrev(
+            _ptr(prev["K_stage"], "prev K_stage", dt, pst), _ptr(prev["V_stage"], "prev V_stage", dt, pst),
+            pw, int(prev["stage_groups"]), int(pcap), int(prev["q0"]), int(prev["q_len"])))
+    _check(_load().hga_stage_routed_from(
+        ctypes.byref(shape), _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
+        _ptr(K, "K", dt, sz["kv"], host_ok=True), _ptr(V, "V", dt, sz["kv"], host_ok=True),
+        _ptr(K_seg, "K_seg", dt, seg, nullable=True), _ptr(V_seg, "V_seg", dt, seg, nullable=True),
+        pp, int(stage_groups), int(cap), _ptr(K_stage, "K_stage", dt, st),
+        _ptr(V_stage, "V_stage", dt, st),
+        _ptr(group_idx_staged, "group_idx_staged", torch.int32, sz["gi"], nullable=True),
+        wp, wb, _stream(stream)), "hga_stage_routed_from")
 
 
 # ------------------------------------------------------------------ compositions

@@ -209,41 +209,90 @@ hga_status hga_attend_bwd(const hga_shape* shape, const void* Q, const void* K, 
                              workspace_bytes, stream);
 }
 
+// Bytes of one per-(b, kv head) list of stage_groups int32 entries, rounded.
+static size_t stage_list_bytes(int32_t batch, int32_t kv_heads, int32_t stage_groups) {
+  return round256((size_t)batch * kv_heads * (size_t)stage_groups * sizeof(int32_t));
+}
+
 hga_status hga_stage_workspace(const hga_shape* shape, int32_t stage_groups, size_t* bytes) {
   hga_status st = hga_validate_shape(shape);
   if (st != HGA_OK) return st;
   if (!bytes) return HGA_ERR_NULL;
   if (stage_groups < 0 || stage_groups % 8 != 0) return HGA_ERR_SHAPE;
-  *bytes = round256((size_t)shape->batch * shape->n_kv_heads * (size_t)stage_groups *
-                    sizeof(int32_t)) +
+  *bytes = 2 * stage_list_bytes(shape->batch, shape->n_kv_heads, stage_groups) +
            round256((size_t)shape->batch * shape->n_kv_heads * sizeof(int32_t));
   return HGA_OK;
+}
+
+// Common checks and launch of the two staging calls.
+static hga_status stage(const hga_shape* shape, const int32_t* group_idx, const void* K,
+                        const void* V, const void* K_seg, const void* V_seg,
+                        const hga_stage_prev* prev, int32_t stage_groups, int32_t stage_capacity,
+                        void* K_stage, void* V_stage, int32_t* group_idx_staged, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!K || !V || !K_stage || !V_stage) return HGA_ERR_NULL;
+  if ((K_seg == nullptr) != (V_seg == nullptr)) return HGA_ERR_NULL;
+  if (shape->top_g > 0 && (!group_idx || !group_idx_staged)) return HGA_ERR_NULL;
+  if (stage_groups % 8 != 0 || stage_groups < hga_stage_min_groups(shape)) return HGA_ERR_SHAPE;
+  if (stage_capacity % HGA_CHUNK != 0 || stage_capacity < 8 * stage_groups + shape->q_len ||
+      stage_capacity > HGA_MAX_KV_LEN)
+    return HGA_ERR_SHAPE;
+  const int32_t q0 = shape->kv_len - shape->q_len;
+  hga::StagePrevD pd{};
+  if (prev) {
+    if (!prev->K_stage || !prev->V_stage || !prev->workspace) return HGA_ERR_NULL;
+    if (prev->stage_groups < 0 || prev->stage_groups % 8 != 0 || prev->q0 < 0 ||
+        prev->q0 % HGA_CHUNK != 0 || prev->q_len < HGA_CHUNK || prev->q_len % HGA_CHUNK != 0 ||
+        prev->q_len > q0 - prev->q0 || prev->stage_capacity % HGA_CHUNK != 0 ||
+        prev->stage_capacity > HGA_MAX_KV_LEN ||
+        prev->stage_capacity < 8 * prev->stage_groups + prev->q_len)
+      return HGA_ERR_SHAPE;
+    pd.Ks = prev->K_stage;
+    pd.Vs = prev->V_stage;
+    pd.ulist = (const int32_t*)prev->workspace;
+    pd.ucount = (const int32_t*)((const uint8_t*)prev->workspace +
+                                 stage_list_bytes(shape->batch, shape->n_kv_heads,
+                                                  prev->stage_groups));
+    pd.sg = prev->stage_groups;
+    pd.Scap = prev->stage_capacity;
+    pd.q0 = prev->q0;
+    pd.Sq = prev->q_len;
+  }
+  size_t need = 0;
+  st = hga_stage_workspace(shape, stage_groups, &need);
+  if (st != HGA_OK) return st;
+  if (!workspace || workspace_bytes < need) return HGA_ERR_WORKSPACE;
+  // unions, then their sizes, then the copy sources of the union slots
+  const size_t lb = stage_list_bytes(shape->batch, shape->n_kv_heads, stage_groups);
+  int32_t* ulist = (int32_t*)workspace;
+  int32_t* ucount = (int32_t*)((uint8_t*)workspace + lb);
+  int32_t* usrc = (int32_t*)((uint8_t*)workspace + lb +
+                             round256((size_t)shape->batch * shape->n_kv_heads * sizeof(int32_t)));
+  return from_hip(hga::launch_stage(dims_of(shape), shape->top_g > 0 ? group_idx : nullptr, K,
+                                    V, K_seg, V_seg, prev ? &pd : nullptr, stage_groups,
+                                    stage_capacity, K_stage, V_stage,
+                                    shape->top_g > 0 ? group_idx_staged : nullptr, ulist,
+                                    ucount, usrc, (hipStream_t)stream));
 }
 
 hga_status hga_stage_routed(const hga_shape* shape, const int32_t* group_idx, const void* K,
                             const void* V, int32_t stage_groups, int32_t stage_capacity,
                             void* K_stage, void* V_stage, int32_t* group_idx_staged,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  hga_status st = hga_validate_shape(shape);
-  if (st != HGA_OK) return st;
-  if (!K || !V || !K_stage || !V_stage) return HGA_ERR_NULL;
-  if (shape->top_g > 0 && (!group_idx || !group_idx_staged)) return HGA_ERR_NULL;
-  if (stage_groups % 8 != 0 || stage_groups < hga_stage_min_groups(shape)) return HGA_ERR_SHAPE;
-  if (stage_capacity % HGA_CHUNK != 0 || stage_capacity < 8 * stage_groups + shape->q_len ||
-      stage_capacity > HGA_MAX_KV_LEN)
-    return HGA_ERR_SHAPE;
-  size_t need = 0;
-  st = hga_stage_workspace(shape, stage_groups, &need);
-  if (st != HGA_OK) return st;
-  if (!workspace || workspace_bytes < need) return HGA_ERR_WORKSPACE;
-  int32_t* ulist = (int32_t*)workspace;
-  int32_t* ucount = (int32_t*)((uint8_t*)workspace +
-                               round256((size_t)shape->batch * shape->n_kv_heads *
-                                        (size_t)stage_groups * sizeof(int32_t)));
-  return from_hip(hga::launch_stage(dims_of(shape), shape->top_g > 0 ? group_idx : nullptr, K,
-                                    V, stage_groups, stage_capacity, K_stage, V_stage,
-                                    shape->top_g > 0 ? group_idx_staged : nullptr, ulist,
-                                    ucount, (hipStream_t)stream));
+  return stage(shape, group_idx, K, V, nullptr, nullptr, nullptr, stage_groups, stage_capacity,
+               K_stage, V_stage, group_idx_staged, workspace, workspace_bytes, stream);
+}
+
+hga_status hga_stage_routed_from(const hga_shape* shape, const int32_t* group_idx, const void* K,
+                                 const void* V, const void* K_seg, const void* V_seg,
+                                 const hga_stage_prev* prev, int32_t stage_groups,
+                                 int32_t stage_capacity, void* K_stage, void* V_stage,
+                                 int32_t* group_idx_staged, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return stage(shape, group_idx, K, V, K_seg, V_seg, prev, stage_groups, stage_capacity,
+               K_stage, V_stage, group_idx_staged, workspace, workspace_bytes, stream);
 }
 
 hga_status hga_decode_route(const hga_shape* shape, const void* Q, const float* chunk_mean,

@@ -46,9 +46,19 @@ hipError_t launch_attend_bwd_dkdv(const Dims& d, const void* Q, const void* K, c
                                   int chunk_end, hipStream_t s);
 
 // The routed working set of a segment staged into a compact buffer (stage.hip).
+// The previous staging of the same history, as the staging kernels read it.
+struct StagePrevD {
+  const void* Ks;          // its staged K, V [B][Hkv][Scap][D]; null: none
+  const void* Vs;
+  const int32_t* ulist;    // its unions [B * Hkv][sg]
+  const int32_t* ucount;   // their sizes [B * Hkv]
+  int sg, Scap, q0, Sq;    // its group slots, rows per (b, kv head), segment start and length
+};
+
 hipError_t launch_stage(const Dims& d, const int32_t* gidx, const void* K, const void* V,
-                        int sg, int scap_s, void* Ks, void* Vs, int32_t* gidx_out,
-                        int32_t* ulist, int32_t* ucount, hipStream_t s);
+                        const void* Kseg, const void* Vseg, const StagePrevD* prev, int sg,
+                        int scap_s, void* Ks, void* Vs, int32_t* gidx_out, int32_t* ulist,
+                        int32_t* ucount, int32_t* usrc, hipStream_t s);
 
 // Decode attention (one query per (b, hq) at position Skv - 1; d.Sq == 1).
 hipError_t launch_decode_attend(const Dims& d, const void* Q, const void* K, const void* V,

@@ -19,6 +19,13 @@
 //                              kv_len - q_len .. kv_len - 1)
 // A routing row's group g maps to its rank in the union when g lies before
 // the segment, else to g - 8 (kv_len - q_len)/64 + sg.
+//
+// Sources of the copies: K / V (typically pinned host memory) by default.
+// Given the previous staging of the same history, a union group that it holds
+// (in its union, or among its segment's rows) is copied from its staged
+// buffers instead, in device memory; given the segment's rows in device
+// memory, those are copied from there.  The bytes staged are the same either
+// way.
 #include "hga_kernels.h"
 #include "hga_device.h"
 
@@ -34,11 +41,16 @@ struct StageP {
   int32_t* gidx_out;     // [B][Hq][nblk][top_g], rewritten
   int32_t* ulist;        // [B * Hkv][sg] the union, ascending
   int32_t* ucount;       // [B * Hkv] its size
+  int32_t* usrc;         // [B * Hkv][sg] first row of each union slot in the previous
+                         // staging, or -1 (copied from K / V)
   const void* K;         // [B][Hkv][Scap][D]
   const void* V;
+  const void* Kseg;      // [B][Hkv][Sq][D] the segment's rows, or null
+  const void* Vseg;
   void* Ks;              // [B][Hkv][Scap_s][D]
   void* Vs;
   int B, Hq, Hkv, nblk, top_g, q0, Sq, Scap, Scap_s, sg, row_bytes;
+  StagePrevD prev;       // prev.Ks == null: no previous staging
 };
 
 // Per (b, kv head): the union of the history groups its rows keep (each row
@@ -48,6 +60,8 @@ struct StageP {
 __global__ __launch_bounds__(kUnionThreads) void stage_union_kernel(const StageP p) {
   __shared__ uint32_t s_bits[kWords];
   __shared__ int s_base[kWords];
+  __shared__ uint32_t s_pbits[kWords];   // the previous staging's union
+  __shared__ int s_pbase[kWords];
   __shared__ int s_wsum[kUnionThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int NW = kUnionThreads / 64;
@@ -55,8 +69,21 @@ __global__ __launch_bounds__(kUnionThreads) void stage_union_kernel(const StageP
   const int r = p.Hq / p.Hkv, nrows = r * p.nblk;
   const int hist = 8 * (p.q0 / kChunk);            // history groups (before the segment)
   const int nwords = (hist + 31) / 32;
-  for (int i = tid; i < kWords; i += kUnionThreads) s_bits[i] = 0;
+  const bool has_prev = p.prev.Ks != nullptr;
+  for (int i = tid; i < kWords; i += kUnionThreads) s_bits[i] = s_pbits[i] = 0;
   __syncthreads();
+  // the previous staging's union, as a bitmap of groups before its segment
+  // (its size clamped to its slots, its entries to its history)
+  const int phist = has_prev ? p.prev.q0 / 8 : 0;
+  if (has_prev) {
+    int pn = p.prev.ucount[bh];
+    pn = pn < 0 ? 0 : (pn > p.prev.sg ? p.prev.sg : pn);
+    const int32_t* pl = p.prev.ulist + (long long)bh * p.prev.sg;
+    for (int i = tid; i < pn; i += kUnionThreads) {
+      const int v = pl[i];
+      if (v >= 0 && v < phist) atomicOr(&s_pbits[v >> 5], 1u << (v & 31));
+    }
+  }
   // one wavefront per row: the row's prefix length, then mark its history groups
   auto row_ptr = [&](int rr) {
     const int hq = hkv * r + rr / p.nblk, blk = rr % p.nblk;
@@ -86,32 +113,51 @@ __global__ __launch_bounds__(kUnionThreads) void stage_union_kernel(const StageP
     }
   }
   __syncthreads();
-  // exclusive prefix of the words' popcounts
-  int cnt = 0;
-  if (tid < kWords) cnt = tid < nwords ? __popc(s_bits[tid]) : 0;
-  // kWords (512) words over the first 8 wavefronts
-  int incl = cnt;
+  // exclusive prefix of the words' popcounts (kWords = 512 words over the
+  // first 8 wavefronts)
+  auto scan = [&](const uint32_t* bits, int nw, int* out) {
+    const int cnt = tid < kWords && tid < nw ? __popc(bits[tid]) : 0;
+    int incl = cnt;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(incl, d);
-    if (lane >= d) incl += u;
-  }
-  if (lane == 63) s_wsum[wv] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int k = 0; k < wv; ++k) base += s_wsum[k];
-  if (tid < kWords) s_base[tid] = base + incl - cnt;
-  int total = 0;
-  for (int k = 0; k < NW; ++k) total += s_wsum[k];
-  __syncthreads();
-  // the union, ascending
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(incl, d);
+      if (lane >= d) incl += u;
+    }
+    if (lane == 63) s_wsum[wv] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int k = 0; k < wv; ++k) base += s_wsum[k];
+    if (tid < kWords) out[tid] = base + incl - cnt;
+    int total = 0;
+    for (int k = 0; k < NW; ++k) total += s_wsum[k];
+    __syncthreads();
+    return total;
+  };
+  const int total = scan(s_bits, nwords, s_base);
+  if (has_prev) scan(s_pbits, (phist + 31) / 32, s_pbase);
+  // the union, ascending, and where each slot's rows are copied from: the
+  // previous staging's segment rows or union slot, else K / V
   int32_t* list = p.ulist + (long long)bh * p.sg;
+  int32_t* src = p.usrc + (long long)bh * p.sg;
+  const int pseg0 = has_prev ? p.prev.q0 / 8 : 0, pseg1 = has_prev ? (p.prev.q0 + p.prev.Sq) / 8 : 0;
   if (tid < nwords) {
     uint32_t m = s_bits[tid];
     int k = s_base[tid];
     while (m) {
       const int bit = __builtin_ctz(m);
-      list[k++] = 32 * tid + bit;
+      const int g = 32 * tid + bit;
+      int from = -1;
+      if (has_prev) {
+        if (g >= pseg0 && g < pseg1) {
+          from = 8 * p.prev.sg + 8 * (g - pseg0);
+        } else if (g < phist && ((s_pbits[g >> 5] >> (g & 31)) & 1u)) {
+          const int rank = s_pbase[g >> 5] + __popc(s_pbits[g >> 5] & ((1u << (g & 31)) - 1u));
+          from = 8 * rank;   // < 8 * prev.sg: at most prev.sg bits are set
+        }
+      }
+      list[k] = g;
+      src[k] = from;
+      ++k;
       m &= m - 1;
     }
   }
@@ -153,6 +199,7 @@ __global__ __launch_bounds__(256) void stage_copy_kernel(const StageP p) {
   const bool uni = j < p.sg / 8;
   const int nslot = uni ? p.ucount[bh] - 8 * j : 8;   // groups of this workgroup present
   const long long kvbase = (long long)bh * p.Scap, sbase = (long long)bh * p.Scap_s;
+  const long long pbase = (long long)bh * p.prev.Scap;
   const int n = p.row_bytes / 64;   // 16-byte pieces per thread: 2, 4 or 8
   uint4 a[8], c[8];
   long long dst[8];
@@ -164,23 +211,43 @@ __global__ __launch_bounds__(256) void stage_copy_kernel(const StageP p) {
     if (i < n) {
       const int o = 16 * (tid + 256 * i);            // byte in the 64-row run
       const int row = o / p.row_bytes, inrow = o % p.row_bytes;
-      long long src_tok, dst_tok;
+      const char* ks;
+      const char* vs;
+      long long dst_tok;
       if (uni) {
         const int slot = 8 * j + row / 8;
         ok[i] = row / 8 < nslot;
-        src_tok = ok[i] ? (long long)p.ulist[(long long)bh * p.sg + slot] * 8 + row % 8 : 0;
+        const long long si = (long long)bh * p.sg + (ok[i] ? slot : 0);
+        const int from = ok[i] ? p.usrc[si] : -1;
+        if (from >= 0) {   // from the previous staging, in device memory
+          const long long off = (pbase + from + row % 8) * p.row_bytes + inrow;
+          ks = reinterpret_cast<const char*>(p.prev.Ks) + off;
+          vs = reinterpret_cast<const char*>(p.prev.Vs) + off;
+        } else {
+          const long long src_tok = ok[i] ? (long long)p.ulist[si] * 8 + row % 8 : 0;
+          const long long off = (kvbase + src_tok) * p.row_bytes + inrow;
+          ks = reinterpret_cast<const char*>(p.K) + off;
+          vs = reinterpret_cast<const char*>(p.V) + off;
+        }
         dst_tok = (long long)slot * 8 + row % 8;
       } else {
         const int t = (j - p.sg / 8) * kChunk + row;
         ok[i] = true;
-        src_tok = (long long)p.q0 + t;
+        if (p.Kseg) {      // the segment's rows, in device memory
+          const long long off = ((long long)bh * p.Sq + t) * p.row_bytes + inrow;
+          ks = reinterpret_cast<const char*>(p.Kseg) + off;
+          vs = reinterpret_cast<const char*>(p.Vseg) + off;
+        } else {
+          const long long off = (kvbase + p.q0 + t) * p.row_bytes + inrow;
+          ks = reinterpret_cast<const char*>(p.K) + off;
+          vs = reinterpret_cast<const char*>(p.V) + off;
+        }
         dst_tok = (long long)p.sg * 8 + t;
       }
-      const long long src = (kvbase + src_tok) * p.row_bytes + inrow;
       dst[i] = (sbase + dst_tok) * p.row_bytes + inrow;
       if (ok[i]) {
-        a[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.K) + src);
-        c[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.V) + src);
+        a[i] = *reinterpret_cast<const uint4*>(ks);
+        c[i] = *reinterpret_cast<const uint4*>(vs);
       }
     }
   }
@@ -195,14 +262,16 @@ __global__ __launch_bounds__(256) void stage_copy_kernel(const StageP p) {
 }  // namespace
 
 hipError_t launch_stage(const Dims& d, const int32_t* gidx, const void* K, const void* V,
-                        int sg, int scap_s, void* Ks, void* Vs, int32_t* gidx_out,
-                        int32_t* ulist, int32_t* ucount, hipStream_t s) {
+                        const void* Kseg, const void* Vseg, const StagePrevD* prev, int sg,
+                        int scap_s, void* Ks, void* Vs, int32_t* gidx_out, int32_t* ulist,
+                        int32_t* ucount, int32_t* usrc, hipStream_t s) {
   StageP p;
-  p.gidx = gidx; p.gidx_out = gidx_out; p.ulist = ulist; p.ucount = ucount;
-  p.K = K; p.V = V; p.Ks = Ks; p.Vs = Vs;
+  p.gidx = gidx; p.gidx_out = gidx_out; p.ulist = ulist; p.ucount = ucount; p.usrc = usrc;
+  p.K = K; p.V = V; p.Kseg = Kseg; p.Vseg = Vseg; p.Ks = Ks; p.Vs = Vs;
   p.B = d.B; p.Hq = d.Hq; p.Hkv = d.Hkv; p.nblk = d.nblk; p.top_g = d.top_g; p.q0 = d.q0;
   p.Sq = d.Sq; p.Scap = d.Scap; p.Scap_s = scap_s; p.sg = sg;
   p.row_bytes = d.D * (d.bf16 ? 2 : 4);
+  p.prev = prev ? *prev : StagePrevD{};
   stage_union_kernel<<<d.B * d.Hkv, kUnionThreads, 0, s>>>(p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

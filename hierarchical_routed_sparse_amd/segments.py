@@ -36,12 +36,16 @@ kernels fetch only the rows they gather (the kept groups, the own chunk, the
 segment's keys for its dK/dV) across the host link.
 
 With ``stage=True`` each segment's routed working set is staged into device
-memory once, after its routing (``hga_stage_routed``): the distinct history
-groups its rows kept and the segment's own rows go into a compact device
-buffer, the routing rows are rewritten against it, and the attention and
-backward run there.  Each kept row then crosses the host link once per
-segment, however many rows gather it; results equal the unstaged ones bit
-for bit.
+memory once, after its routing (``hga_stage_routed_from``): the distinct
+history groups its rows kept and the segment's own rows go into a compact
+device buffer, the routing rows are rewritten against it, and the attention
+and backward run there.  Two such buffers alternate: a group that the
+previous segment's staging already holds (in its union or among its own
+rows) is copied from there, in device memory, so only the groups no earlier
+staging held cross the host link.  When ``step`` is given the segment's keys
+and values in device memory (``K_seg``, ``V_seg``: the active segment, as a
+projection produces it), the segment's rows are staged from those.  Results
+equal the unstaged ones bit for bit.
 """
 from __future__ import annotations
 
@@ -50,7 +54,7 @@ from dataclasses import dataclass
 
 from . import (CHUNK, hga_attend_bwd_dkdv_range, hga_attend_bwd_dq, hga_attend_bwd_workspace,
                hga_attend_fwd, hga_build_summaries, hga_route, hga_route_causal,
-               hga_stage_min_groups, hga_stage_routed, hga_stage_workspace, make_shape)
+               hga_stage_min_groups, hga_stage_routed_from, hga_stage_workspace, make_shape)
 
 
 @dataclass
@@ -105,20 +109,24 @@ class SegmentRunner:
         self.workspace = torch.empty(hga_attend_bwd_workspace(self.shape(self.nseg - 1)),
                                      dtype=torch.uint8, device=device)
         self.stage = stage
+        self._cur = 0
+        self._last_staged = -1   # segment staged last (a staging source only for the next one)
         if stage:
             # the staged history of the last segment is the largest the bound
             # allows: every history group, or every row's top_g
             sg_max = max(hga_stage_min_groups(self.shape(i)) for i in range(self.nseg))
             self.stage_cap = -(-(8 * sg_max + seg_len) // 64) * 64
             st = (batch, n_kv_heads, self.stage_cap, head_dim)
-            self.k_stage = torch.empty(st, dtype=elt, device=device)
-            self.v_stage = torch.empty(st, dtype=elt, device=device)
+            # two staging buffers, segments alternate between them; each
+            # segment's staging copies from the other what it already holds
+            self.k_stages = [torch.empty(st, dtype=elt, device=device) for _ in range(2)]
+            self.v_stages = [torch.empty(st, dtype=elt, device=device) for _ in range(2)]
             self.dk_stage = torch.empty(st, dtype=elt, device=device)
             self.dv_stage = torch.empty(st, dtype=elt, device=device)
             self.group_idx_staged = torch.empty_like(self.group_idx)
-            self.stage_ws = torch.empty(max(256, hga_stage_workspace(self.shape(self.nseg - 1),
-                                                                     sg_max)),
-                                        dtype=torch.uint8, device=device)
+            self.stage_wss = [torch.empty(max(256, hga_stage_workspace(self.shape(self.nseg - 1),
+                                                                       sg_max)),
+                                          dtype=torch.uint8, device=device) for _ in range(2)]
             big = make_shape(batch, n_q_heads, n_kv_heads, head_dim, seg_len, self.stage_cap,
                              top_k, top_g, dtype=dtype, softmax_scale=softmax_scale)
             self.workspace = torch.empty(max(self.workspace.numel(),
@@ -139,8 +147,17 @@ class SegmentRunner:
                           dtype=self.dtype, softmax_scale=self.scale,
                           kv_capacity=self.stage_cap)
 
-    def forward(self, i: int, Q, stream=None):
-        """Steps 1-3 for segment i (its keys/values already in the history)."""
+    @property
+    def k_stage(self):
+        return self.k_stages[self._cur]
+
+    @property
+    def v_stage(self):
+        return self.v_stages[self._cur]
+
+    def forward(self, i: int, Q, stream=None, K_seg=None, V_seg=None):
+        """Steps 1-3 for segment i (its keys/values already in the history;
+        with ``stage``, K_seg / V_seg optionally the same rows in device memory)."""
         s = self.shape(i)
         c0, c1 = i * self.S // CHUNK, (i + 1) * self.S // CHUNK
         hga_build_summaries(s, self.k_history, self.chunk_mean, self.group_mean, c0, c1,
@@ -152,9 +169,20 @@ class SegmentRunner:
             hga_route(s, Q, self.chunk_mean, self.group_mean, self.chunk_idx, self.group_idx,
                       stream=stream)
         if self.stage:
-            hga_stage_routed(s, self.group_idx, self.k_history, self.v_history,
-                             self.stage_groups[i], self.k_stage, self.v_stage,
-                             self.group_idx_staged, self.stage_ws, stream=stream)
+            cur = i % 2
+            prev = None
+            if i > 0 and self._last_staged == i - 1:
+                # the previous segment's staging, in the other buffer
+                prev = dict(K_stage=self.k_stages[1 - cur], V_stage=self.v_stages[1 - cur],
+                            workspace=self.stage_wss[1 - cur],
+                            stage_groups=self.stage_groups[i - 1], q0=(i - 1) * self.S,
+                            q_len=self.S)
+            self._cur = cur
+            hga_stage_routed_from(s, self.group_idx, self.k_history, self.v_history,
+                                  self.stage_groups[i], self.k_stage, self.v_stage,
+                                  self.group_idx_staged, self.stage_wss[cur], K_seg=K_seg,
+                                  V_seg=V_seg, prev=prev, stream=stream)
+            self._last_staged = i
             hga_attend_fwd(self.staged_shape(i), Q, self.k_stage, self.v_stage,
                            self.group_idx_staged, self.O, self.lse, stream=stream)
         else:
@@ -193,8 +221,8 @@ class SegmentRunner:
                                   self.group_idx, c0, c1, self.dK, self.dV, self.workspace,
                                   stream=stream)
 
-    def step(self, i: int, Q, dO, stream=None) -> SegmentResult:
-        self.forward(i, Q, stream)
+    def step(self, i: int, Q, dO, stream=None, K_seg=None, V_seg=None) -> SegmentResult:
+        self.forward(i, Q, stream, K_seg=K_seg, V_seg=V_seg)
         self.backward(i, Q, dO, stream)
         rows = slice(i * self.S, (i + 1) * self.S)
         return SegmentResult(self.O, self.lse, self.group_idx, self.dQ,

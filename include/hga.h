@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 8
+#define HGA_ABI_VERSION 9
 #define HGA_CHUNK 64      /* tokens per chunk (the page's 64-token chunks) */
 #define HGA_GROUP 8       /* tokens per group (the page's 8-token groups)  */
 #define HGA_QBLOCK 64     /* queries per routing block                      */
@@ -299,14 +299,58 @@ hga_status hga_attend_bwd_dkdv_range(const hga_shape* shape, const void* Q, cons
  *                     its rank in the union, a group of the segment ->
  *                     g - 8 (kv_len - q_len)/64 + stage_groups, -1 padded
  *   workspace         hga_stage_workspace(shape, stage_groups) bytes: the
- *                     unions ([B][Hkv][stage_groups] int32) and their sizes
- *                     ([B][Hkv] int32) */
+ *                     unions ([B][Hkv][stage_groups] int32), their sizes
+ *                     ([B][Hkv] int32) and the copy sources of the union slots
+ *                     ([B][Hkv][stage_groups] int32), each rounded up to 256
+ *                     bytes */
 int32_t hga_stage_min_groups(const hga_shape* shape);   /* -1 for an invalid shape */
 hga_status hga_stage_workspace(const hga_shape* shape, int32_t stage_groups, size_t* bytes);
 hga_status hga_stage_routed(const hga_shape* shape, const int32_t* group_idx, const void* K,
                             const void* V, int32_t stage_groups, int32_t stage_capacity,
                             void* K_stage, void* V_stage, int32_t* group_idx_staged,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* The previous staging of the same history (the segment before, routed and
+ * staged by hga_stage_routed or hga_stage_routed_from), as its caller holds it. */
+typedef struct {
+  const void* K_stage;      /* its K_stage, V_stage (device), still unchanged       */
+  const void* V_stage;
+  const void* workspace;    /* its workspace (its unions and their sizes)           */
+  int32_t stage_groups;     /* its stage_groups                                     */
+  int32_t stage_capacity;   /* its stage_capacity                                   */
+  int32_t q0;               /* its segment's first position (its kv_len - q_len)    */
+  int32_t q_len;            /* its segment's length                                 */
+} hga_stage_prev;
+
+/* hga_stage_routed with other sources for the same bytes (page "BMW's 16 GB
+ * GPU just did what needs an A100", section "What HGA does differently",
+ * memory paragraph: the active segment stays in GPU memory; and consecutive
+ * segments share most of their routed working set).  K_stage, V_stage, group_idx_staged and the
+ * workspace's unions are exactly those hga_stage_routed writes; only where
+ * the rows are copied from differs:
+ *   - a union group that the previous staging holds (in its union, or among
+ *     its segment's rows) is copied from prev->K_stage / prev->V_stage, in
+ *     device memory, instead of from K / V;
+ *   - the segment's own rows come from K_seg / V_seg when they are given:
+ *     [B][Hkv][q_len][D] dtype, device memory, equal to K's / V's rows
+ *     kv_len - q_len .. kv_len - 1;
+ *   - every other row comes from K / V as in hga_stage_routed.
+ * prev may be NULL (no previous staging); K_seg and V_seg are both NULL or
+ * both given.  prev must describe a staging of the same history for the same
+ * batch, heads, head_dim and dtype, whose buffers have not been written
+ * since: 0 <= prev->stage_groups, a multiple of 8; prev->q0 and prev->q_len
+ * multiples of 64, prev->q_len >= 64, prev->q0 + prev->q_len <= kv_len -
+ * q_len; prev->stage_capacity a multiple of 64 in [8 * prev->stage_groups +
+ * prev->q_len, HGA_MAX_KV_LEN].  A prev that breaks the first condition gives
+ * unspecified staged values but never a read outside prev->K_stage /
+ * prev->V_stage (ranks are clamped to the sizes given).  The workspace is
+ * hga_stage_workspace(shape, stage_groups) bytes, as for hga_stage_routed. */
+hga_status hga_stage_routed_from(const hga_shape* shape, const int32_t* group_idx, const void* K,
+                                 const void* V, const void* K_seg, const void* V_seg,
+                                 const hga_stage_prev* prev, int32_t stage_groups,
+                                 int32_t stage_capacity, void* K_stage, void* V_stage,
+                                 int32_t* group_idx_staged, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* Decode: attention of one new token per (b, query head) over a resident
  * key/value cache (page section "What HGA does differently", read for

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert hga.hga_abi_version() == 8
+    assert hga.hga_abi_version() == 9
 
 
 def _ok_shape(**kw):
@@ -214,3 +214,49 @@ def test_zero_budget_routing_launches_nothing(lib):
     # with a budget, the missing Q_prev is still an argument error
     s = _ok_shape(top_k=4, top_g=0)
     assert lib.hga_route_causal(ctypes.byref(s), fake, None, fake, None, fake, None, None) == 1
+
+
+def test_stage_argument_errors(lib):
+    """Both staging calls reject bad arguments before launching anything
+    (bogus non-null pointers are never dereferenced on these paths)."""
+    s = _ok_shape()
+    SP = ctypes.POINTER(hga.HgaShape)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.hga_stage_min_groups.argtypes = [SP]
+    lib.hga_stage_workspace.argtypes = [SP, i32, ctypes.POINTER(sz)]
+    lib.hga_stage_routed.argtypes = [SP, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.hga_stage_routed_from.argtypes = [SP, vp, vp, vp, vp, vp, ctypes.POINTER(hga.HgaStagePrev),
+                                          i32, i32, vp, vp, vp, vp, sz, vp]
+    sg = lib.hga_stage_min_groups(ctypes.byref(s))
+    assert sg == 8 * 1792 // 8 and sg % 8 == 0   # every history group (14336 tokens)
+    cap = -(-(8 * sg + s.q_len) // 64) * 64
+    n = sz(0)
+    assert lib.hga_stage_workspace(ctypes.byref(s), sg, ctypes.byref(n)) == 0
+    r256 = lambda x: -(-x // 256) * 256
+    assert n.value == 2 * r256(8 * sg * 4) + r256(8 * 4)   # unions, sizes, copy sources
+    assert lib.hga_stage_workspace(ctypes.byref(s), sg + 4, ctypes.byref(n)) == 2
+    need = n.value
+    ok = [16, 16, 16]
+    stage = lambda *a: lib.hga_stage_routed(ctypes.byref(s), *a)
+    assert stage(16, None, 16, sg, cap, 16, 16, 16, 16, need, None) == 1
+    assert stage(16, 16, 16, sg + 4, cap, 16, 16, 16, 16, need, None) == 2
+    assert stage(16, 16, 16, sg - 8, cap, 16, 16, 16, 16, need, None) == 2
+    assert stage(16, 16, 16, sg, cap - 64, 16, 16, 16, 16, need, None) == 2
+    assert stage(16, 16, 16, sg, cap, 16, 16, 16, 16, need - 1, None) == 4
+
+    def frm(kseg, vseg, prev, ws=need):
+        return lib.hga_stage_routed_from(ctypes.byref(s), *ok, kseg, vseg,
+                                         ctypes.byref(prev) if prev else None, sg, cap,
+                                         16, 16, 16, 16, ws, None)
+    good = dict(K_stage=16, V_stage=16, workspace=16, stage_groups=8 * 1536, q0=12288,
+                q_len=2048, stage_capacity=8 * 8 * 1536 + 2048)
+    P = lambda **kw: hga.HgaStagePrev(**{**good, **kw})
+    assert frm(16, None, None) == 1                        # K_seg without V_seg
+    assert frm(16, 16, P(), need - 1) == 4                 # otherwise valid: workspace short
+    assert frm(None, None, P(workspace=None)) == 1
+    assert frm(None, None, P(V_stage=None)) == 1
+    assert frm(None, None, P(stage_groups=12)) == 2        # not a multiple of 8
+    assert frm(None, None, P(q0=12288 + 64)) == 2          # its segment runs into this one
+    assert frm(None, None, P(q0=100)) == 2                 # not chunk aligned
+    assert frm(None, None, P(q_len=0)) == 2
+    assert frm(None, None, P(stage_capacity=8 * 8 * 1536 + 2048 - 64)) == 2

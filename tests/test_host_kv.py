@@ -60,17 +60,20 @@ def test_segments_with_host_kv_match_device():
             assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("name,L,S,k,g,on_host", [
-    ("stage_dev", 1024, 256, 3, 12, False),
-    ("stage_host", 1024, 256, 3, 12, True),
+@pytest.mark.parametrize("name,L,S,k,g,on_host,seg_dev", [
+    ("stage_dev", 1024, 256, 3, 12, False, False),
+    ("stage_host", 1024, 256, 3, 12, True, False),
+    # the active segment's keys and values also in device memory
+    ("stage_host_segdev", 1024, 256, 3, 12, True, True),
     # budgets that keep more groups than the history holds for early segments
     # and fewer than it for late ones: the union bounded both ways
-    ("stage_host_wide", 2048, 256, 20, 150, True),
+    ("stage_host_wide", 2048, 256, 20, 150, True, False),
 ])
-def test_staged_working_set_matches_unstaged(name, L, S, k, g, on_host):
+def test_staged_working_set_matches_unstaged(name, L, S, k, g, on_host, seg_dev):
     """Segment-wise training with each segment's routed working set staged
-    into a compact device buffer gives, segment by segment, the unstaged
-    results bit for bit (O, lse, routing, dQ, the segment's dK and dV)."""
+    into a compact device buffer (from the previous segment's staging where it
+    holds a group) gives, segment by segment, the unstaged results bit for bit
+    (O, lse, routing, dQ, the segment's dK and dV)."""
     from gpu_common import DEV
     print(f"[case] {name}", flush=True)
     w = syn.Workload(name, 1, 4, 2, 128, L, L, k, g, "bf16", 43, 1 / math.sqrt(128),
@@ -86,10 +89,66 @@ def test_staged_working_set_matches_unstaged(name, L, S, k, g, on_host):
         seg = []
         for i in range(L // S):
             rows = slice(i * S, (i + 1) * S)
-            r = run.step(i, t["Q"][:, :, rows].contiguous(), t["dO"][:, :, rows].contiguous())
+            kv = {}
+            if staged and seg_dev:
+                kv = dict(K_seg=t["K"][:, :, rows].contiguous(), V_seg=t["V"][:, :, rows].contiguous())
+            r = run.step(i, t["Q"][:, :, rows].contiguous(), t["dO"][:, :, rows].contiguous(), **kv)
             torch.cuda.synchronize()
             seg.append([v.clone() for v in (r.O, r.lse, r.group_idx, r.dQ, r.dK, r.dV)])
         outs.append(seg)
     for i, (a, b) in enumerate(zip(outs[0], outs[1])):
         for nm, u, v in zip(("O", "lse", "group_idx", "dQ", "dK", "dV"), a, b):
             assert torch.equal(u, v), (i, nm)
+
+
+def test_stage_from_previous_writes_what_plain_staging_writes():
+    """hga_stage_routed_from (previous staging and device segment rows as
+    sources) writes the same staged rows, unions and rewritten routing rows
+    as hga_stage_routed from the history alone, segment after segment; and
+    from the second segment on most union groups are copied from the previous
+    staging."""
+    from gpu_common import DEV
+    L, S, k, g = 2048, 256, 6, 40
+    print("[case] stage_from L2048 S256", flush=True)
+    w = syn.Workload("stage_from", 1, 4, 2, 128, L, L, k, g, "bf16", 44, 1 / math.sqrt(128),
+                     backward=True)
+    x = syn.make_inputs(w, with_grad_output=True)
+    t = {kk: syn.to_torch(v, "bf16", DEV) for kk, v in x.items()}
+    run = SegmentRunner(1, 4, 2, 128, L, S, k, g, device=DEV, kv_on_host=True, stage=True)
+    run.k_history.copy_(t["K"].cpu())
+    run.v_history.copy_(t["V"].cpu())
+    kst = torch.empty_like(run.k_stages[0])
+    vst = torch.empty_like(run.v_stages[0])
+    gis = torch.empty_like(run.group_idx_staged)
+    ws = torch.empty_like(run.stage_wss[0])
+    nbh = 2
+    for i in range(L // S):
+        rows = slice(i * S, (i + 1) * S)
+        run.forward(i, t["Q"][:, :, rows].contiguous(), K_seg=t["K"][:, :, rows].contiguous(),
+                    V_seg=t["V"][:, :, rows].contiguous())
+        s = run.shape(i)
+        sg = run.stage_groups[i]
+        hga.hga_stage_routed(s, run.group_idx, run.k_history, run.v_history, sg, kst, vst, gis, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(gis, run.group_idx_staged), i
+        lb = -(-(nbh * sg * 4) // 256) * 256
+        cw = run.stage_wss[i % 2]
+        cnt = cw[lb:lb + 4 * nbh].view(torch.int32).cpu()
+        assert torch.equal(cnt, ws[lb:lb + 4 * nbh].view(torch.int32).cpu()), i
+        ul_a = cw[:4 * nbh * sg].view(torch.int32).view(nbh, sg).cpu()
+        ul_b = ws[:4 * nbh * sg].view(torch.int32).view(nbh, sg).cpu()
+        src = cw[lb + 256:][:4 * nbh * sg].view(torch.int32).view(nbh, sg).cpu()
+        from_prev = 0
+        for h in range(nbh):
+            n = int(cnt[h])
+            assert torch.equal(ul_a[h, :n], ul_b[h, :n]), (i, h)
+            written = list(range(8 * n)) + list(range(8 * sg, 8 * sg + S))
+            assert torch.equal(run.k_stage[0, h, written], kst[0, h, written]), (i, h)
+            assert torch.equal(run.v_stage[0, h, written], vst[0, h, written]), (i, h)
+            from_prev += int((src[h, :n] >= 0).sum())
+            if i == 0:
+                assert int((src[h, :n] >= 0).sum()) == 0
+        if i >= 2:
+            # the previous staging held the previous segment and most of the
+            # history before it
+            assert from_prev > 0.5 * int(cnt.sum()), (i, from_prev, int(cnt.sum()))
