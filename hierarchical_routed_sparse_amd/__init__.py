@@ -24,7 +24,7 @@ import os
 
 __all__ = [
     "HGAError", "HgaShape", "make_shape", "lib_path", "hga_abi_version", "hga_validate_shape",
-    "hga_build_summaries", "hga_route", "hga_route_causal", "hga_attend_fwd", "hga_attend_bwd_workspace",
+    "hga_build_summaries", "hga_build_summaries_rows", "hga_route", "hga_route_causal", "hga_attend_fwd", "hga_attend_bwd_workspace",
     "hga_attend_bwd", "hga_attend_bwd_noalloc", "hga_attend_bwd_prep", "hga_attend_bwd_dq", "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range",
     "hga_validate_decode_shape", "hga_decode", "hga_decode_route", "hga_decode_attend",
     "hga_decode_route_causal", "hga_stage_min_groups", "hga_stage_workspace", "hga_stage_routed",
@@ -111,6 +111,7 @@ def _load(path: str = None):
     lib.hga_decode_route.argtypes = [_SP] + [_vp] * 6
     lib.hga_decode_attend.argtypes = [_SP] + [_vp] * 7
     lib.hga_decode_route_causal.argtypes = [_SP] + [_vp] * 6
+    lib.hga_build_summaries_rows.argtypes = [_SP, _vp, i32, i32, _vp, _vp, i32, i32, _vp]
     lib.hga_stage_min_groups.argtypes = [_SP]
     lib.hga_stage_min_groups.restype = ctypes.c_int32
     lib.hga_stage_workspace.argtypes = [_SP, i32, ctypes.POINTER(sz)]
@@ -124,7 +125,7 @@ def _load(path: str = None):
                  "hga_attend_bwd_prep",
                  "hga_attend_bwd_dq",
                  "hga_attend_bwd_dkdv", "hga_attend_bwd_dkdv_range", "hga_stage_workspace",
-                 "hga_stage_routed", "hga_stage_routed_from"):
+                 "hga_stage_routed", "hga_stage_routed_from", "hga_build_summaries_rows"):
         getattr(lib, name).restype = ctypes.c_int
     _libs[path] = lib
     return lib
@@ -446,6 +447,22 @@ def hga_decode_attend(shape, Q, K, V, group_idx, O, lse=None, stream=None):
         _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
         _ptr(O, "O", dt, sz["q"]), _ptr(lse, "lse", torch.float32, sz["lse"], nullable=True),
         _stream(stream)), "hga_decode_attend")
+
+
+def hga_build_summaries_rows(shape, K_rows, row0, chunk_mean, group_mean, chunk_begin,
+                             chunk_end, stream=None):
+    """Summaries of chunks [chunk_begin, chunk_end) from K_rows [B, Hkv, rows, D]
+    holding positions row0 .. row0 + rows - 1 (see include/hga.h)."""
+    import torch
+    sz = _sizes(shape)
+    rows = K_rows.shape[2]
+    _check(_load().hga_build_summaries_rows(
+        ctypes.byref(shape),
+        _ptr(K_rows, "K_rows", _elt_dtype(shape), (shape.batch, shape.n_kv_heads, rows,
+                                                   shape.head_dim), host_ok=True),
+        int(row0), int(rows), _ptr(chunk_mean, "chunk_mean", torch.float32, sz["cm"]),
+        _ptr(group_mean, "group_mean", torch.float32, sz["gm"]), int(chunk_begin),
+        int(chunk_end), _stream(stream)), "hga_build_summaries_rows")
 
 
 def hga_stage_min_groups(shape) -> int:

@@ -74,8 +74,27 @@ hga_status hga_build_summaries(const hga_shape* shape, const void* K, float* chu
   if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > shape->kv_len / HGA_CHUNK)
     return HGA_ERR_SHAPE;
   if (chunk_end == chunk_begin) return HGA_OK;
-  return from_hip(hga::launch_summaries(dims_of(shape), K, chunk_mean, group_mean, chunk_begin,
+  const hga::Dims d = dims_of(shape);
+  return from_hip(hga::launch_summaries(d, K, d.Scap, 0, chunk_mean, group_mean, chunk_begin,
                                         chunk_end, (hipStream_t)stream));
+}
+
+hga_status hga_build_summaries_rows(const hga_shape* shape, const void* K_rows, int32_t row0,
+                                    int32_t rows, float* chunk_mean, float* group_mean,
+                                    int32_t chunk_begin, int32_t chunk_end, void* stream) {
+  hga_status st = shape && shape->q_len == 1 ? hga_validate_decode_shape(shape)
+                                             : hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!K_rows || !chunk_mean || !group_mean) return HGA_ERR_NULL;
+  if (row0 < 0 || row0 % HGA_CHUNK != 0 || rows <= 0 || rows % HGA_CHUNK != 0 ||
+      rows > shape->kv_len - row0)
+    return HGA_ERR_SHAPE;
+  if (chunk_begin < row0 / HGA_CHUNK || chunk_end < chunk_begin ||
+      chunk_end > (row0 + rows) / HGA_CHUNK)
+    return HGA_ERR_SHAPE;
+  if (chunk_end == chunk_begin) return HGA_OK;
+  return from_hip(hga::launch_summaries(dims_of(shape), K_rows, rows, row0, chunk_mean,
+                                        group_mean, chunk_begin, chunk_end, (hipStream_t)stream));
 }
 
 hga_status hga_route(const hga_shape* shape, const void* Q, const float* chunk_mean,

@@ -16,8 +16,10 @@ struct Dims {
   bool bf16;
 };
 
-hipError_t launch_summaries(const Dims& d, const void* K, float* chunk_mean, float* group_mean,
-                            int chunk_begin, int chunk_end, hipStream_t s);
+// K holds kcap rows per (b, kv head), for positions row0 .. row0 + kcap - 1
+// (the whole capacity: kcap = d.Scap, row0 = 0).
+hipError_t launch_summaries(const Dims& d, const void* K, int kcap, int row0, float* chunk_mean,
+                            float* group_mean, int chunk_begin, int chunk_end, hipStream_t s);
 
 // causal: route block j with the mean of the 64 queries before it (Q_prev
 // [B][Hq][64][D] = the 64 queries before the segment, for its first block).

@@ -17,10 +17,10 @@ namespace hga {
 namespace {
 
 struct SumP {
-  const void* K;
+  const void* K;       // [B][Hkv][Kcap][D]: positions row0 .. row0 + Kcap - 1
   float* cm;
   float* gm;
-  int Scap, chunk_begin, chunk_end, nslots, nwork;   // Scap: rows per (b, kv head)
+  int Scap, Kcap, row0, chunk_begin, chunk_end, nslots, nwork;   // Scap: summary capacity
 };
 
 template <typename T, int D>
@@ -44,7 +44,8 @@ __global__ __launch_bounds__(kThreads) void summaries_kernel(const SumP p) {
   for (int e = 0; e < 8; ++e) s[e] = 0.f;
   if (live) {
     Pair<T> x;
-    load_pair(x, reinterpret_cast<const T*>(p.K) + ((long long)bh * p.Scap + chunk * kChunk + 4 * q) * D + 8 * o, D);
+    load_pair(x, reinterpret_cast<const T*>(p.K) +
+                     ((long long)bh * p.Kcap + chunk * kChunk - p.row0 + 4 * q) * D + 8 * o, D);
     const T* r = reinterpret_cast<const T*>(&x);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -76,10 +77,12 @@ __global__ __launch_bounds__(kThreads) void summaries_kernel(const SumP p) {
 }
 
 template <typename T, int D>
-hipError_t run(const Dims& d, const void* K, float* cm, float* gm, int cb, int ce, hipStream_t s) {
+hipError_t run(const Dims& d, const void* K, int kcap, int row0, float* cm, float* gm, int cb,
+               int ce, hipStream_t s) {
   constexpr int kCpw = kThreads / (16 * (D / 8));
   SumP p;
-  p.K = K; p.cm = cm; p.gm = gm; p.Scap = d.Scap; p.chunk_begin = cb; p.chunk_end = ce;
+  p.K = K; p.cm = cm; p.gm = gm; p.Scap = d.Scap; p.Kcap = kcap; p.row0 = row0;
+  p.chunk_begin = cb; p.chunk_end = ce;
   p.nslots = (ce - cb + kCpw - 1) / kCpw;
   p.nwork = d.B * d.Hkv * p.nslots;
   if (p.nwork == 0) return hipSuccess;
@@ -89,13 +92,13 @@ hipError_t run(const Dims& d, const void* K, float* cm, float* gm, int cb, int c
 
 }  // namespace
 
-hipError_t launch_summaries(const Dims& d, const void* K, float* chunk_mean, float* group_mean,
-                            int chunk_begin, int chunk_end, hipStream_t s) {
+hipError_t launch_summaries(const Dims& d, const void* K, int kcap, int row0, float* chunk_mean,
+                            float* group_mean, int chunk_begin, int chunk_end, hipStream_t s) {
   if (d.bf16)
-    return d.D == 128 ? run<uint16_t, 128>(d, K, chunk_mean, group_mean, chunk_begin, chunk_end, s)
-                      : run<uint16_t, 64>(d, K, chunk_mean, group_mean, chunk_begin, chunk_end, s);
-  return d.D == 128 ? run<float, 128>(d, K, chunk_mean, group_mean, chunk_begin, chunk_end, s)
-                    : run<float, 64>(d, K, chunk_mean, group_mean, chunk_begin, chunk_end, s);
+    return d.D == 128 ? run<uint16_t, 128>(d, K, kcap, row0, chunk_mean, group_mean, chunk_begin, chunk_end, s)
+                      : run<uint16_t, 64>(d, K, kcap, row0, chunk_mean, group_mean, chunk_begin, chunk_end, s);
+  return d.D == 128 ? run<float, 128>(d, K, kcap, row0, chunk_mean, group_mean, chunk_begin, chunk_end, s)
+                    : run<float, 64>(d, K, kcap, row0, chunk_mean, group_mean, chunk_begin, chunk_end, s);
 }
 
 }  // namespace hga

@@ -44,7 +44,8 @@ previous segment's staging already holds (in its union or among its own
 rows) is copied from there, in device memory, so only the groups no earlier
 staging held cross the host link.  When ``step`` is given the segment's keys
 and values in device memory (``K_seg``, ``V_seg``: the active segment, as a
-projection produces it), the segment's rows are staged from those.  Results
+projection produces it), the segment's summaries are built and its rows
+staged from those.  Results
 equal the unstaged ones bit for bit.
 """
 from __future__ import annotations
@@ -53,8 +54,9 @@ import contextlib
 from dataclasses import dataclass
 
 from . import (CHUNK, hga_attend_bwd_dkdv_range, hga_attend_bwd_dq, hga_attend_bwd_workspace,
-               hga_attend_fwd, hga_build_summaries, hga_route, hga_route_causal,
-               hga_stage_min_groups, hga_stage_routed_from, hga_stage_workspace, make_shape)
+               hga_attend_fwd, hga_build_summaries, hga_build_summaries_rows, hga_route,
+               hga_route_causal, hga_stage_min_groups, hga_stage_routed_from,
+               hga_stage_workspace, make_shape)
 
 
 @dataclass
@@ -157,11 +159,17 @@ class SegmentRunner:
 
     def forward(self, i: int, Q, stream=None, K_seg=None, V_seg=None):
         """Steps 1-3 for segment i (its keys/values already in the history;
-        with ``stage``, K_seg / V_seg optionally the same rows in device memory)."""
+        K_seg / V_seg optionally the same rows in device memory, from which the
+        segment's summaries and, with ``stage``, its staged rows are taken)."""
         s = self.shape(i)
         c0, c1 = i * self.S // CHUNK, (i + 1) * self.S // CHUNK
-        hga_build_summaries(s, self.k_history, self.chunk_mean, self.group_mean, c0, c1,
-                            stream=stream)
+        if K_seg is not None:
+            # the segment's summaries from its rows in device memory
+            hga_build_summaries_rows(s, K_seg, i * self.S, self.chunk_mean, self.group_mean,
+                                     c0, c1, stream=stream)
+        else:
+            hga_build_summaries(s, self.k_history, self.chunk_mean, self.group_mean, c0, c1,
+                                stream=stream)
         if self.causal:
             hga_route_causal(s, Q, self.q_prev if i > 0 else None, self.chunk_mean,
                              self.group_mean, self.chunk_idx, self.group_idx, stream=stream)

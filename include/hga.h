@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 9
+#define HGA_ABI_VERSION 10
 #define HGA_CHUNK 64      /* tokens per chunk (the page's 64-token chunks) */
 #define HGA_GROUP 8       /* tokens per group (the page's 8-token groups)  */
 #define HGA_QBLOCK 64     /* queries per routing block                      */
@@ -122,6 +122,18 @@ hga_status hga_validate_decode_shape(const hga_shape* shape);
 hga_status hga_build_summaries(const hga_shape* shape, const void* K, float* chunk_mean,
                                float* group_mean, int32_t chunk_begin, int32_t chunk_end,
                                void* stream);
+
+/* hga_build_summaries with the keys read from a buffer that holds a range of
+ * positions only (same page passage; for the active segment in GPU memory
+ * while the history lives in host RAM):
+ *   K_rows     [B][Hkv][rows][D] dtype: positions row0 .. row0 + rows - 1;
+ *              row0 >= 0 and rows > 0 multiples of 64, row0 + rows <= kv_len
+ *   [chunk_begin, chunk_end) within [row0 / 64, (row0 + rows) / 64)
+ * The summaries are written exactly as hga_build_summaries writes them from
+ * a K holding the same keys at those positions. */
+hga_status hga_build_summaries_rows(const hga_shape* shape, const void* K_rows, int32_t row0,
+                                    int32_t rows, float* chunk_mean, float* group_mean,
+                                    int32_t chunk_begin, int32_t chunk_end, void* stream);
 
 /* Two-level routing (page section "What HGA does differently": score the
  * chunk summaries, keep the top-k chunks, open them at group level, keep the

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert hga.hga_abi_version() == 9
+    assert hga.hga_abi_version() == 10
 
 
 def _ok_shape(**kw):
@@ -260,3 +260,22 @@ def test_stage_argument_errors(lib):
     assert frm(None, None, P(q0=100)) == 2                 # not chunk aligned
     assert frm(None, None, P(q_len=0)) == 2
     assert frm(None, None, P(stage_capacity=8 * 8 * 1536 + 2048 - 64)) == 2
+
+
+def test_summaries_rows_argument_errors(lib):
+    """The row-range summaries call rejects ranges that the buffer does not
+    hold, before launching anything."""
+    s = _ok_shape()
+    SP = ctypes.POINTER(hga.HgaShape)
+    i32, vp = ctypes.c_int32, ctypes.c_void_p
+    lib.hga_build_summaries_rows.argtypes = [SP, vp, i32, i32, vp, vp, i32, i32, vp]
+    f = lambda *a: lib.hga_build_summaries_rows(ctypes.byref(s), *a)
+    assert f(None, 14336, 2048, 16, 16, 224, 256, None) == 1
+    assert f(16, 14336, 2048, None, 16, 224, 256, None) == 1
+    assert f(16, 14300, 2048, 16, 16, 224, 256, None) == 2      # row0 not chunk aligned
+    assert f(16, 14336, 2000, 16, 16, 224, 256, None) == 2      # rows not a multiple of 64
+    assert f(16, 14336, 4096, 16, 16, 224, 256, None) == 2      # past kv_len
+    assert f(16, 14336, 2048, 16, 16, 223, 256, None) == 2      # chunk before the buffer
+    assert f(16, 14336, 2048, 16, 16, 224, 257, None) == 2      # chunk past the buffer
+    assert f(16, 14336, 2048, 16, 16, 230, 229, None) == 2
+    assert f(16, 14336, 2048, 16, 16, 230, 230, None) == 0      # empty range: nothing launched

@@ -227,6 +227,31 @@ def test_incremental_summaries_match_full_build():
     assert torch.equal(full_c, inc_c) and torch.equal(full_g, inc_g)
 
 
+@pytest.mark.parametrize("name", ["bf16_seg_b2", "fp32_d128", "bf16_d64"])
+def test_summaries_from_a_row_range_match_full_build(name):
+    """hga_build_summaries_rows over a buffer holding a range of positions
+    writes, for the chunks in that range, exactly what the full build writes,
+    and nothing outside them."""
+    w = SMALL[name]
+    x = syn.make_inputs(w)
+    t = upload(x, w.dtype)
+    s = shape_of(w)
+    n, D = w.kv_len // 64, w.head_dim
+    full_c = torch.empty(w.batch, w.n_kv_heads, n, D, device=DEV)
+    full_g = torch.empty(w.batch, w.n_kv_heads, n * 8, D, device=DEV)
+    hga.hga_build_summaries(s, t["K"], full_c, full_g)
+    row0, rows = 64 * (n // 3), 64 * (n - n // 3)
+    part = t["K"][:, :, row0:row0 + rows].contiguous()
+    inc_c = torch.full_like(full_c, float("nan"))
+    inc_g = torch.full_like(full_g, float("nan"))
+    c0, c1 = row0 // 64 + 1, n
+    hga.hga_build_summaries_rows(s, part, row0, inc_c, inc_g, c0, c1)
+    torch.cuda.synchronize()
+    assert torch.equal(full_c[:, :, c0:c1], inc_c[:, :, c0:c1])
+    assert torch.equal(full_g[:, :, 8 * c0:8 * c1], inc_g[:, :, 8 * c0:8 * c1])
+    assert torch.isnan(inc_c[:, :, :c0]).all() and torch.isnan(inc_g[:, :, :8 * c0]).all()
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 _cache = {}
