@@ -89,9 +89,10 @@ __global__ __launch_bounds__(kUnionThreads) void stage_union_kernel(const StageP
     const int hq = hkv * r + rr / p.nblk, blk = rr % p.nblk;
     return (((long long)b * p.Hq + hq) * p.nblk + blk) * p.top_g;
   };
-  auto prefix_len = [&](const int32_t* g, int limit) {
+  // prefix length of a row from entry i0s on (entries before i0s valid)
+  auto prefix_from = [&](const int32_t* g, int limit, int i0s) {
     int n = p.top_g;
-    for (int i0 = 0; i0 < p.top_g; i0 += 64) {
+    for (int i0 = i0s; i0 < p.top_g; i0 += 64) {
       const int i = i0 + lane;
       const int v = i < p.top_g ? g[i] : 0;
       const int prev = i > 0 && i < p.top_g ? g[i - 1] : -1;
@@ -103,13 +104,45 @@ __global__ __launch_bounds__(kUnionThreads) void stage_union_kernel(const StageP
     }
     return n;
   };
-  for (int rr = wv; rr < nrows; rr += NW) {
-    const int32_t* g = p.gidx + row_ptr(rr);
-    const int limit = 8 * (p.q0 / kChunk + rr % p.nblk);
-    const int n = prefix_len(g, limit);
-    for (int i = lane; i < n; i += 64) {
-      const int v = g[i];
-      if (v < hist) atomicOr(&s_bits[v >> 5], 1u << (v & 31));
+  // Rows rr0, rr0 + NW, ... (kRowBatch of them, this wavefront's): the first
+  // 64 entries of each are loaded together (one load per lane and row, all
+  // in flight at once), with each row's prefix length; entries past the 64th
+  // are read row by row where a row has them.
+  constexpr int kRowBatch = 8;
+  auto load_rows = [&](int rr0, int (&v)[kRowBatch], int (&n)[kRowBatch]) {
+#pragma unroll
+    for (int k = 0; k < kRowBatch; ++k) {
+      const int rr = rr0 + NW * k;
+      v[k] = rr < nrows && lane < p.top_g ? p.gidx[row_ptr(rr) + lane] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kRowBatch; ++k) {
+      const int rr = rr0 + NW * k;
+      n[k] = 0;
+      if (rr < nrows) {
+        const int limit = 8 * (p.q0 / kChunk + rr % p.nblk);
+        const int up = __shfl_up(v[k], 1);
+        const int prev = lane == 0 ? -1 : up;
+        const uint64_t bad =
+            __ballot(lane < p.top_g && (v[k] < 0 || v[k] >= limit || v[k] <= prev));
+        n[k] = bad ? (int)__builtin_ctzll(bad)
+                   : prefix_from(p.gidx + row_ptr(rr), limit, 64);
+      }
+    }
+  };
+  for (int rr0 = wv; rr0 < nrows; rr0 += NW * kRowBatch) {
+    int v[kRowBatch], n[kRowBatch];
+    load_rows(rr0, v, n);
+#pragma unroll
+    for (int k = 0; k < kRowBatch; ++k) {
+      if (lane < n[k] && v[k] < hist) atomicOr(&s_bits[v[k] >> 5], 1u << (v[k] & 31));
+      if (n[k] > 64) {
+        const int32_t* g = p.gidx + row_ptr(rr0 + NW * k);
+        for (int i = 64 + lane; i < n[k]; i += 64) {
+          const int x = g[i];
+          if (x < hist) atomicOr(&s_bits[x >> 5], 1u << (x & 31));
+        }
+      }
     }
   }
   __syncthreads();
@@ -164,23 +197,24 @@ __global__ __launch_bounds__(kUnionThreads) void stage_union_kernel(const StageP
   if (tid == 0) p.ucount[bh] = total;
   // every row rewritten against the staged layout
   const int seg0 = hist;   // first group of the segment
-  for (int rr = wv; rr < nrows; rr += NW) {
-    const long long o = row_ptr(rr);
-    const int32_t* g = p.gidx + o;
-    const int limit = 8 * (p.q0 / kChunk + rr % p.nblk);
-    const int n = prefix_len(g, limit);
-    for (int i = lane; i < p.top_g; i += 64) {
-      int v = -1;
-      if (i < n) {
-        const int x = g[i];
-        if (x < seg0) {
-          const uint32_t w = s_bits[x >> 5];
-          v = s_base[x >> 5] + __popc(w & ((1u << (x & 31)) - 1u));
-        } else {
-          v = x - seg0 + p.sg;
-        }
-      }
-      p.gidx_out[o + i] = v;
+  auto staged = [&](int x) -> int {
+    if (x < seg0) {
+      const uint32_t w = s_bits[x >> 5];
+      return s_base[x >> 5] + (int)__popc(w & ((1u << (x & 31)) - 1u));
+    }
+    return x - seg0 + p.sg;
+  };
+  for (int rr0 = wv; rr0 < nrows; rr0 += NW * kRowBatch) {
+    int v[kRowBatch], n[kRowBatch];
+    load_rows(rr0, v, n);
+#pragma unroll
+    for (int k = 0; k < kRowBatch; ++k) {
+      const int rr = rr0 + NW * k;
+      if (rr >= nrows) continue;
+      const long long o = row_ptr(rr);
+      if (lane < p.top_g) p.gidx_out[o + lane] = lane < n[k] ? staged(v[k]) : -1;
+      for (int i = 64 + lane; i < p.top_g; i += 64)
+        p.gidx_out[o + i] = i < n[k] ? staged(p.gidx[o + i]) : -1;
     }
   }
 }
