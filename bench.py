@@ -500,6 +500,63 @@ def calibration_copy(dev):
     del src, dst
 
 
+def replay_percentiles(g, steps: int) -> dict:
+    """Per-step time distribution of `steps` further replays of `g`, each
+    bracketed by HIP events on the replay stream (after the timed region, so
+    the events do not touch it): p10, median, p90 in ms."""
+    import torch
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(st)
+        g.replay()
+        b.record(st)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    q = lambda f: t[min(len(t) - 1, int(f * (len(t) - 1) + 0.5))]
+    return {"p10": round(q(0.1), 4), "p50": round(q(0.5), 4), "p90": round(q(0.9), 4)}
+
+
+def device_measured(dev) -> dict:
+    """What this GPU reports and sustains, beside the published peaks the
+    rooflines use: device properties, the rate of a plain 1 GiB device copy
+    (read plus write bytes over time), and the rate of a large dense bf16
+    matrix product through the vendor library (torch.matmul, 8192^3)."""
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "memory_GB": round(p.total_memory / 1e9, 1),
+            "l2_MB": round(getattr(p, "L2_cache_size", 0) / 2 ** 20, 1)}
+    st = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    src = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    sec = timed(lambda: dst.copy_(src), 10)
+    info["copy_GBs"] = round(2 * 2 ** 30 / sec / 1e9, 1)
+    del src, dst
+    n = 8192
+    x = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    y = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    sec = timed(lambda: torch.matmul(x, y), 10)
+    info["bf16_gemm_TFLOPs"] = round(2 * n ** 3 / sec / 1e12, 1)
+    del x, y
+    torch.cuda.empty_cache()
+    return info
+
+
 def decode_work(w, kept_groups: int) -> dict:
     """Per-launch algorithmic bytes of the two decode kernels.  Routing: the
     queries, the chunk summaries before the own chunk (read once for the query
@@ -859,6 +916,7 @@ def main():
     ms_step = ms_serial
     if g_side is not None:
         ms_step = timed_replays(g_side, args.steps, args.warmup)
+    step_pct = replay_percentiles(g_side if g_side is not None else g_serial, args.steps)
 
     dom = max(phases, key=lambda p: phase_rep[p]["kernel_us"])
     kind, amount = work[dom]
@@ -958,6 +1016,8 @@ def main():
         },
         "roofline": roof,
         "phases": phase_rep,
+        "step_ms_percentiles": step_pct,
+        "device": device_measured(dev),
         "cpu_baseline": base,
     }
     print(json.dumps(out))
