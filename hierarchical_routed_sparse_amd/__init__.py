@@ -73,7 +73,8 @@ _SP = ctypes.POINTER(HgaShape)
 class HgaStagePrev(ctypes.Structure):
     """hga_stage_prev of include/hga.h: the previous staging of the same history."""
     _fields_ = [("K_stage", ctypes.c_void_p), ("V_stage", ctypes.c_void_p),
-                ("workspace", ctypes.c_void_p), ("stage_groups", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("stage_groups", ctypes.c_int32),
                 ("stage_capacity", ctypes.c_int32), ("q0", ctypes.c_int32),
                 ("q_len", ctypes.c_int32)]
 
@@ -512,10 +513,10 @@ def hga_stage_routed_from(shape, group_idx, K, V, stage_groups, K_stage, V_stage
     if prev is not None:
         pcap = prev["K_stage"].shape[2]
         pst = (shape.batch, shape.n_kv_heads, pcap, shape.head_dim)
-        pw, _ = _ws(prev["workspace"])
+        pw, pwb = _ws(prev["workspace"])
         pp = ctypes.byref(HgaStagePrev(
             _ptr(prev["K_stage"], "prev K_stage", dt, pst), _ptr(prev["V_stage"], "prev V_stage", dt, pst),
-            pw, int(prev["stage_groups"]), int(pcap), int(prev["q0"]), int(prev["q_len"])))
+            pw, pwb, int(prev["stage_groups"]), int(pcap), int(prev["q0"]), int(prev["q_len"])))
     _check(_load().hga_stage_routed_from(
         ctypes.byref(shape), _ptr(group_idx, "group_idx", torch.int32, sz["gi"], nullable=True),
         _ptr(K, "K", dt, sz["kv"], host_ok=True), _ptr(V, "V", dt, sz["kv"], host_ok=True),

@@ -268,6 +268,11 @@ static hga_status stage(const hga_shape* shape, const int32_t* group_idx, const 
         prev->stage_capacity > HGA_MAX_KV_LEN ||
         prev->stage_capacity < 8 * prev->stage_groups + prev->q_len)
       return HGA_ERR_SHAPE;
+    // its unions and their sizes are read
+    if (prev->workspace_bytes <
+        stage_list_bytes(shape->batch, shape->n_kv_heads, prev->stage_groups) +
+            round256((size_t)shape->batch * shape->n_kv_heads * sizeof(int32_t)))
+      return HGA_ERR_WORKSPACE;
     pd.Ks = prev->K_stage;
     pd.Vs = prev->V_stage;
     pd.ulist = (const int32_t*)prev->workspace;

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HGA_ABI_VERSION 10
+#define HGA_ABI_VERSION 11
 #define HGA_CHUNK 64      /* tokens per chunk (the page's 64-token chunks) */
 #define HGA_GROUP 8       /* tokens per group (the page's 8-token groups)  */
 #define HGA_QBLOCK 64     /* queries per routing block                      */
@@ -328,6 +328,7 @@ typedef struct {
   const void* K_stage;      /* its K_stage, V_stage (device), still unchanged       */
   const void* V_stage;
   const void* workspace;    /* its workspace (its unions and their sizes)           */
+  size_t workspace_bytes;   /* that workspace's size in bytes                       */
   int32_t stage_groups;     /* its stage_groups                                     */
   int32_t stage_capacity;   /* its stage_capacity                                   */
   int32_t q0;               /* its segment's first position (its kv_len - q_len)    */
@@ -353,9 +354,12 @@ typedef struct {
  * since: 0 <= prev->stage_groups, a multiple of 8; prev->q0 and prev->q_len
  * multiples of 64, prev->q_len >= 64, prev->q0 + prev->q_len <= kv_len -
  * q_len; prev->stage_capacity a multiple of 64 in [8 * prev->stage_groups +
- * prev->q_len, HGA_MAX_KV_LEN].  A prev that breaks the first condition gives
- * unspecified staged values but never a read outside prev->K_stage /
- * prev->V_stage (ranks are clamped to the sizes given).  The workspace is
+ * prev->q_len, HGA_MAX_KV_LEN]; prev->workspace_bytes at least the unions and
+ * sizes parts of a staging workspace for prev->stage_groups (HGA_ERR_WORKSPACE
+ * otherwise).  A prev whose buffers do not hold what that staging wrote
+ * gives unspecified staged values but never a read outside prev->K_stage,
+ * prev->V_stage and the workspace_bytes of prev->workspace (sizes and ranks
+ * are clamped to the stage_groups given).  The workspace is
  * hga_stage_workspace(shape, stage_groups) bytes, as for hga_stage_routed. */
 hga_status hga_stage_routed_from(const hga_shape* shape, const int32_t* group_idx, const void* K,
                                  const void* V, const void* K_seg, const void* V_seg,

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert hga.hga_abi_version() == 10
+    assert hga.hga_abi_version() == 11
 
 
 def _ok_shape(**kw):
@@ -248,8 +248,10 @@ def test_stage_argument_errors(lib):
         return lib.hga_stage_routed_from(ctypes.byref(s), *ok, kseg, vseg,
                                          ctypes.byref(prev) if prev else None, sg, cap,
                                          16, 16, 16, 16, ws, None)
-    good = dict(K_stage=16, V_stage=16, workspace=16, stage_groups=8 * 1536, q0=12288,
-                q_len=2048, stage_capacity=8 * 8 * 1536 + 2048)
+    pneed = r256(8 * 8 * 1536 * 4) + r256(8 * 4)   # its unions and sizes
+    good = dict(K_stage=16, V_stage=16, workspace=16, workspace_bytes=pneed,
+                stage_groups=8 * 1536, q0=12288, q_len=2048,
+                stage_capacity=8 * 8 * 1536 + 2048)
     P = lambda **kw: hga.HgaStagePrev(**{**good, **kw})
     assert frm(16, None, None) == 1                        # K_seg without V_seg
     assert frm(16, 16, P(), need - 1) == 4                 # otherwise valid: workspace short
@@ -260,6 +262,7 @@ def test_stage_argument_errors(lib):
     assert frm(None, None, P(q0=100)) == 2                 # not chunk aligned
     assert frm(None, None, P(q_len=0)) == 2
     assert frm(None, None, P(stage_capacity=8 * 8 * 1536 + 2048 - 64)) == 2
+    assert frm(None, None, P(workspace_bytes=pneed - 1)) == 4   # its unions would be overread
 
 
 def test_summaries_rows_argument_errors(lib):
