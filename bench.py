@@ -1017,7 +1017,8 @@ def main():
         "roofline": roof,
         "phases": phase_rep,
         "step_ms_percentiles": step_pct,
-        "device": device_measured(dev),
+        # (not in the counter runs, whose calibration copy must be the only large one)
+        "device": None if args.calibrate_copy else device_measured(dev),
         "cpu_baseline": base,
     }
     print(json.dumps(out))
