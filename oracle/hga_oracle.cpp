@@ -23,7 +23,7 @@
  *
  * Return codes: 0 ok, 2 bad shape, 3 invalid routing indices, 4 non-finite input.
  *
- * Readings taken where the page is silent (each is listed in the design notes):
+ * Readings taken where the page is silent:
  *  - summary of a chunk (and of a group) = mean of its keys;
  *  - the query side of the routing score = mean of the block's C queries
  *    (strictly causal variant: mean of the C queries before the block);
