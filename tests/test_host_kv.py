@@ -60,18 +60,21 @@ def test_segments_with_host_kv_match_device():
             assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("name,B,L,S,k,g,on_host,seg_dev", [
-    ("stage_dev", 1, 1024, 256, 3, 12, False, False),
-    ("stage_host", 1, 1024, 256, 3, 12, True, False),
+@pytest.mark.parametrize("name,B,L,S,k,g,on_host,seg_dev,causal", [
+    ("stage_dev", 1, 1024, 256, 3, 12, False, False, False),
+    ("stage_host", 1, 1024, 256, 3, 12, True, False, False),
     # the active segment's keys and values also in device memory
-    ("stage_host_segdev", 1, 1024, 256, 3, 12, True, True),
+    ("stage_host_segdev", 1, 1024, 256, 3, 12, True, True, False),
     # two sequences: every (b, kv head) has its own union and sources
-    ("stage_host_segdev_b2", 2, 768, 256, 4, 20, True, True),
+    ("stage_host_segdev_b2", 2, 768, 256, 4, 20, True, True, False),
+    # strictly causal routing (each segment's first block routed with the
+    # previous segment's last 64 queries)
+    ("stage_host_segdev_causal", 1, 1024, 256, 3, 12, True, True, True),
     # budgets that keep more groups than the history holds for early segments
     # and fewer than it for late ones: the union bounded both ways
-    ("stage_host_wide", 1, 2048, 256, 20, 150, True, False),
+    ("stage_host_wide", 1, 2048, 256, 20, 150, True, False, False),
 ])
-def test_staged_working_set_matches_unstaged(name, B, L, S, k, g, on_host, seg_dev):
+def test_staged_working_set_matches_unstaged(name, B, L, S, k, g, on_host, seg_dev, causal):
     """Segment-wise training with each segment's routed working set staged
     into a compact device buffer (from the previous segment's staging where it
     holds a group) gives, segment by segment, the unstaged results bit for bit
@@ -85,7 +88,7 @@ def test_staged_working_set_matches_unstaged(name, B, L, S, k, g, on_host, seg_d
     outs = []
     for staged in (False, True):
         run = SegmentRunner(B, 4, 2, 128, L, S, k, g, device=DEV,
-                            kv_on_host=on_host and staged, stage=staged)
+                            kv_on_host=on_host and staged, stage=staged, causal=causal)
         run.k_history.copy_(t["K"].cpu() if (on_host and staged) else t["K"])
         run.v_history.copy_(t["V"].cpu() if (on_host and staged) else t["V"])
         seg = []
