@@ -254,7 +254,10 @@ static hga_status stage(const hga_shape* shape, const int32_t* group_idx, const 
   if (!K || !V || !K_stage || !V_stage) return HGA_ERR_NULL;
   if ((K_seg == nullptr) != (V_seg == nullptr)) return HGA_ERR_NULL;
   if (shape->top_g > 0 && (!group_idx || !group_idx_staged)) return HGA_ERR_NULL;
-  if (stage_groups % 8 != 0 || stage_groups < hga_stage_min_groups(shape)) return HGA_ERR_SHAPE;
+  // (group counts bounded before they are multiplied: no shape accepted can overflow)
+  if (stage_groups % 8 != 0 || stage_groups < hga_stage_min_groups(shape) ||
+      stage_groups > HGA_MAX_KV_LEN / 8)
+    return HGA_ERR_SHAPE;
   if (stage_capacity % HGA_CHUNK != 0 || stage_capacity < 8 * stage_groups + shape->q_len ||
       stage_capacity > HGA_MAX_KV_LEN)
     return HGA_ERR_SHAPE;
@@ -262,7 +265,8 @@ static hga_status stage(const hga_shape* shape, const int32_t* group_idx, const 
   hga::StagePrevD pd{};
   if (prev) {
     if (!prev->K_stage || !prev->V_stage || !prev->workspace) return HGA_ERR_NULL;
-    if (prev->stage_groups < 0 || prev->stage_groups % 8 != 0 || prev->q0 < 0 ||
+    if (prev->stage_groups < 0 || prev->stage_groups % 8 != 0 ||
+        prev->stage_groups > HGA_MAX_KV_LEN / 8 || prev->q0 < 0 ||
         prev->q0 % HGA_CHUNK != 0 || prev->q_len < HGA_CHUNK || prev->q_len % HGA_CHUNK != 0 ||
         prev->q_len > q0 - prev->q0 || prev->stage_capacity % HGA_CHUNK != 0 ||
         prev->stage_capacity > HGA_MAX_KV_LEN ||

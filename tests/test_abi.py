@@ -243,6 +243,7 @@ def test_stage_argument_errors(lib):
     assert stage(16, 16, 16, sg - 8, cap, 16, 16, 16, 16, need, None) == 2
     assert stage(16, 16, 16, sg, cap - 64, 16, 16, 16, 16, need, None) == 2
     assert stage(16, 16, 16, sg, cap, 16, 16, 16, 16, need - 1, None) == 4
+    assert stage(16, 16, 16, 1 << 28, cap, 16, 16, 16, 16, need, None) == 2   # 8x would overflow
 
     def frm(kseg, vseg, prev, ws=need):
         return lib.hga_stage_routed_from(ctypes.byref(s), *ok, kseg, vseg,
@@ -263,6 +264,7 @@ def test_stage_argument_errors(lib):
     assert frm(None, None, P(q_len=0)) == 2
     assert frm(None, None, P(stage_capacity=8 * 8 * 1536 + 2048 - 64)) == 2
     assert frm(None, None, P(workspace_bytes=pneed - 1)) == 4   # its unions would be overread
+    assert frm(None, None, P(stage_groups=1 << 28)) == 2        # 8x would overflow
 
 
 def test_summaries_rows_argument_errors(lib):
