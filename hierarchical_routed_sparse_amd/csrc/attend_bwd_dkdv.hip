@@ -188,6 +188,11 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
   const int kin = 16 * wv + l16;         // this lane's key within the chunk
   const uint32_t mygroups = 3u << (2 * wv);
 
+  // the first entry list's mask words are read first: the list then waits on
+  // those loads alone, not on the K and V loads issued after them
+  EntryMasks<> em;
+  load_entry_masks(p, b, hkv, c, 0, em);
+
   // this wavefront's 16 keys as B operands of S = Q . K^T and dP = dO . V^T
   Frag<T> kf[D / 32], vf[D / 32];
   {
@@ -247,7 +252,8 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_dkdv_kernel(const DkvP p)
 
   for (int r0 = 0; r0 < nrows; r0 += kRowsPerPass) {
     // ---- entry list for routing rows [r0, r0 + kRowsPerPass)
-    const int nent = build_entries(p, b, hkv, c, r0, s_ent, s_wsum);
+    if (r0 > 0) load_entry_masks(p, b, hkv, c, r0, em);
+    const int nent = build_entries(p, r0, em, s_ent, s_wsum);
     if (nent == 0) continue;
 
     // ---- walk the entries, S - 1 of them in flight
