@@ -134,27 +134,31 @@ __device__ __forceinline__ void dq_order_block(const DqP& p, int bh, int* s_mem)
 
 // The routing row's entry of the group-mask map: byte c = mask of the row's
 // kept groups in chunk c (bit t = group 8c + t), for every chunk of the
-// history, from the row's kept groups in s_glist (ascending, nvalid of them).
-// s_cm: nchunks bytes of LDS.  Every thread of the workgroup must call it.
+// history, from the row's kept groups in s_glist (nvalid of them).  Built in
+// LDS as little-endian 32-bit words: group g is bit g & 31 of word g >> 5
+// (byte g >> 3, bit g & 7), set with one atomic OR per kept group.  s_cm:
+// nchunks bytes of 4-byte aligned LDS.  Every thread of the workgroup must
+// call it.
 template <typename P>
 __device__ __forceinline__ void write_cmask_row(const P& p, long long row, int nvalid,
-                                                const int* s_glist, uint8_t* s_cm) {
+                                                const int* s_glist, uint32_t* s_cm) {
   const int tid = threadIdx.x;
   const int nch = p.Skv / kChunk;
-  for (int i = tid; i < nch; i += kThreads) s_cm[i] = 0;
+  for (int i = tid; i < (nch + 3) / 4; i += kThreads) s_cm[i] = 0;
   __syncthreads();
-  // the last kept group of each chunk (the list is ascending) ORs the run
   for (int i = tid; i < nvalid; i += kThreads) {
-    const int ch = s_glist[i] >> 3;
-    if (i + 1 == nvalid || (s_glist[i + 1] >> 3) != ch) {
-      uint32_t m = 0;
-      for (int j = i; j >= 0 && (s_glist[j] >> 3) == ch; --j) m |= 1u << (s_glist[j] & 7);
-      s_cm[ch] = (uint8_t)m;
-    }
+    const int g = s_glist[i];
+    atomicOr(&s_cm[g >> 5], 1u << (g & 31));
   }
   __syncthreads();
   uint8_t* out = p.cmask + row * nch;
-  for (int i = tid; i < nch; i += kThreads) out[i] = s_cm[i];
+  if ((nch & 3) == 0) {
+    // whole words: every row starts 4-byte aligned (the map is)
+    for (int i = tid; i < nch / 4; i += kThreads) reinterpret_cast<uint32_t*>(out)[i] = s_cm[i];
+  } else {
+    const uint8_t* s8 = reinterpret_cast<const uint8_t*>(s_cm);
+    for (int i = tid; i < nch; i += kThreads) out[i] = s8[i];
+  }
 }
 
 // bf16: the register budget is held to four wavefronts per SIMD (4
@@ -397,7 +401,7 @@ void attend_bwd_dq_kernel(const DqP p) {
   // once every wave is past them)
   if (p.cmask) {
     __syncthreads();
-    write_cmask_row(p, row, nvalid, s_glist, reinterpret_cast<uint8_t*>(smem));
+    write_cmask_row(p, row, nvalid, s_glist, reinterpret_cast<uint32_t*>(smem));
   }
   const float sc = p.scale;
   if constexpr (sizeof(T) == 2) {
@@ -464,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void attend_bwd_prep_kernel(const DqP p) 
   }
   const int nvalid = load_routing_prefix<kThreads>(p.gidx + row * p.top_g, p.top_g, cb * 8,
                                                    s_glist, s_wsum);
-  write_cmask_row(p, row, nvalid, s_glist, reinterpret_cast<uint8_t*>(s_mem));
+  write_cmask_row(p, row, nvalid, s_glist, reinterpret_cast<uint32_t*>(s_mem));
 }
 
 template <typename T, int D>
