@@ -5,11 +5,14 @@
 #include <math.h>
 #include <string.h>
 
-// (the host-only checks -- hga_validate_shape, hga_validate_decode_shape,
-// hga_status_str, hga_abi_version, hga_stage_min_groups -- are in
-// hga_validate.cpp, plain C++ that the CPU tests also build with sanitizers)
+// (the host-only entry points -- hga_validate_shape, hga_validate_decode_shape,
+// hga_status_str, hga_abi_version, hga_stage_min_groups and the workspace
+// sizes -- are in hga_validate.cpp, and the workspace layouts and the staging
+// checks in hga_layout.h: plain C++ that the CPU tests also build with
+// sanitizers)
 
 #include "hga_kernels.h"
+#include "hga_layout.h"
 
 namespace {
 
@@ -33,26 +36,10 @@ hga::Dims dims_of(const hga_shape* s) {
 
 hga_status from_hip(hipError_t e) { return e == hipSuccess ? HGA_OK : HGA_ERR_HIP; }
 
-size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+using hga_layout::cmask_bytes;
+using hga_layout::delta_bytes;
+using hga_layout::order_bytes;
 
-// workspace: delta (fp32 per query row), then the group-mask map (one byte per
-// (routing row, chunk)), then two dK/dV work orders (one int per (b, kv head,
-// chunk) each): the full range's, written by the dQ call, and a sub-range's,
-// written by the range call itself (so a range call never spoils the other)
-size_t delta_bytes(const hga_shape* s) {
-  return round256((size_t)s->batch * s->n_q_heads * s->q_len * sizeof(float));
-}
-size_t cmask_bytes(const hga_shape* s) {
-  return round256((size_t)s->batch * s->n_q_heads * (s->q_len / HGA_QBLOCK) *
-                  (s->kv_len / HGA_CHUNK));
-}
-// the dK/dV work order: one int per (b, kv head, chunk)
-size_t order_bytes(const hga_shape* s) {
-  return round256((size_t)s->batch * s->n_kv_heads * (s->kv_len / HGA_CHUNK) * sizeof(int32_t));
-}
-size_t workspace_bytes(const hga_shape* s) {
-  return delta_bytes(s) + cmask_bytes(s) + 2 * order_bytes(s);
-}
 int32_t* order_full(const hga_shape* s, void* ws) {
   return (int32_t*)((uint8_t*)ws + delta_bytes(s) + cmask_bytes(s));
 }
@@ -139,14 +126,6 @@ hga_status hga_attend_fwd(const hga_shape* shape, const void* Q, const void* K, 
                                          (hipStream_t)stream));
 }
 
-hga_status hga_attend_bwd_workspace(const hga_shape* shape, size_t* bytes) {
-  hga_status st = hga_validate_shape(shape);
-  if (st != HGA_OK) return st;
-  if (!bytes) return HGA_ERR_NULL;
-  *bytes = workspace_bytes(shape);
-  return HGA_OK;
-}
-
 hga_status hga_attend_bwd_dq(const hga_shape* shape, const void* Q, const void* K,
                              const void* V, const void* O, const float* lse, const void* dO,
                              const int32_t* group_idx, void* dQ, void* workspace,
@@ -160,7 +139,7 @@ hga_status hga_attend_bwd_dq(const hga_shape* shape, const void* Q, const void* 
     return from_hip(hga::launch_attend_bwd_dq(dims_of(shape), Q, K, V, O, lse, dO, group_idx,
                                               dQ, nullptr, nullptr, nullptr,
                                               (hipStream_t)stream));
-  if (!workspace || workspace_bytes < ::workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < hga_layout::bwd_workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
   return from_hip(hga::launch_attend_bwd_dq(
       dims_of(shape), Q, K, V, O, lse, dO, group_idx, dQ, (float*)workspace,
       (uint8_t*)workspace + delta_bytes(shape), order_full(shape, workspace),
@@ -174,7 +153,7 @@ hga_status hga_attend_bwd_prep(const hga_shape* shape, const void* O, const void
   if (st != HGA_OK) return st;
   if (!O || !dO) return HGA_ERR_NULL;
   if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
-  if (!workspace || workspace_bytes < ::workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < hga_layout::bwd_workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
   return from_hip(hga::launch_attend_bwd_prep(
       dims_of(shape), O, dO, group_idx, (float*)workspace,
       (uint8_t*)workspace + delta_bytes(shape), order_full(shape, workspace),
@@ -190,7 +169,7 @@ hga_status hga_attend_bwd_dkdv_range(const hga_shape* shape, const void* Q, cons
   if (st != HGA_OK) return st;
   if (!Q || !K || !V || !lse || !dO || !dK || !dV) return HGA_ERR_NULL;
   if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
-  if (!workspace || workspace_bytes < ::workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < hga_layout::bwd_workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
   if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > shape->kv_len / HGA_CHUNK)
     return HGA_ERR_SHAPE;
   if (chunk_end == chunk_begin) return HGA_OK;
@@ -220,27 +199,12 @@ hga_status hga_attend_bwd(const hga_shape* shape, const void* Q, const void* K, 
   if (st != HGA_OK) return st;
   if (!Q || !K || !V || !O || !lse || !dO || !dQ || !dK || !dV) return HGA_ERR_NULL;
   if (shape->top_g > 0 && !group_idx) return HGA_ERR_NULL;
-  if (!workspace || workspace_bytes < ::workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < hga_layout::bwd_workspace_bytes(shape)) return HGA_ERR_WORKSPACE;
   st = hga_attend_bwd_dq(shape, Q, K, V, O, lse, dO, group_idx, dQ, workspace, workspace_bytes,
                          stream);
   if (st != HGA_OK) return st;
   return hga_attend_bwd_dkdv(shape, Q, K, V, lse, dO, group_idx, dK, dV, workspace,
                              workspace_bytes, stream);
-}
-
-// Bytes of one per-(b, kv head) list of stage_groups int32 entries, rounded.
-static size_t stage_list_bytes(int32_t batch, int32_t kv_heads, int32_t stage_groups) {
-  return round256((size_t)batch * kv_heads * (size_t)stage_groups * sizeof(int32_t));
-}
-
-hga_status hga_stage_workspace(const hga_shape* shape, int32_t stage_groups, size_t* bytes) {
-  hga_status st = hga_validate_shape(shape);
-  if (st != HGA_OK) return st;
-  if (!bytes) return HGA_ERR_NULL;
-  if (stage_groups < 0 || stage_groups % 8 != 0) return HGA_ERR_SHAPE;
-  *bytes = 2 * stage_list_bytes(shape->batch, shape->n_kv_heads, stage_groups) +
-           round256((size_t)shape->batch * shape->n_kv_heads * sizeof(int32_t));
-  return HGA_OK;
 }
 
 // Common checks and launch of the two staging calls.
@@ -254,50 +218,29 @@ static hga_status stage(const hga_shape* shape, const int32_t* group_idx, const 
   if (!K || !V || !K_stage || !V_stage) return HGA_ERR_NULL;
   if ((K_seg == nullptr) != (V_seg == nullptr)) return HGA_ERR_NULL;
   if (shape->top_g > 0 && (!group_idx || !group_idx_staged)) return HGA_ERR_NULL;
-  // (group counts bounded before they are multiplied: no shape accepted can overflow)
-  if (stage_groups % 8 != 0 || stage_groups < hga_stage_min_groups(shape) ||
-      stage_groups > HGA_MAX_KV_LEN / 8)
-    return HGA_ERR_SHAPE;
-  if (stage_capacity % HGA_CHUNK != 0 || stage_capacity < 8 * stage_groups + shape->q_len ||
-      stage_capacity > HGA_MAX_KV_LEN)
-    return HGA_ERR_SHAPE;
-  const int32_t q0 = shape->kv_len - shape->q_len;
+  st = hga_layout::check_stage_args(shape, stage_groups, stage_capacity, prev);
+  if (st != HGA_OK) return st;
   hga::StagePrevD pd{};
   if (prev) {
-    if (!prev->K_stage || !prev->V_stage || !prev->workspace) return HGA_ERR_NULL;
-    if (prev->stage_groups < 0 || prev->stage_groups % 8 != 0 ||
-        prev->stage_groups > HGA_MAX_KV_LEN / 8 || prev->q0 < 0 ||
-        prev->q0 % HGA_CHUNK != 0 || prev->q_len < HGA_CHUNK || prev->q_len % HGA_CHUNK != 0 ||
-        prev->q_len > q0 - prev->q0 || prev->stage_capacity % HGA_CHUNK != 0 ||
-        prev->stage_capacity > HGA_MAX_KV_LEN ||
-        prev->stage_capacity < 8 * prev->stage_groups + prev->q_len)
-      return HGA_ERR_SHAPE;
-    // its unions and their sizes are read
-    if (prev->workspace_bytes <
-        stage_list_bytes(shape->batch, shape->n_kv_heads, prev->stage_groups) +
-            round256((size_t)shape->batch * shape->n_kv_heads * sizeof(int32_t)))
-      return HGA_ERR_WORKSPACE;
     pd.Ks = prev->K_stage;
     pd.Vs = prev->V_stage;
     pd.ulist = (const int32_t*)prev->workspace;
     pd.ucount = (const int32_t*)((const uint8_t*)prev->workspace +
-                                 stage_list_bytes(shape->batch, shape->n_kv_heads,
-                                                  prev->stage_groups));
+                                 hga_layout::stage_list_bytes(shape->batch, shape->n_kv_heads,
+                                                              prev->stage_groups));
     pd.sg = prev->stage_groups;
     pd.Scap = prev->stage_capacity;
     pd.q0 = prev->q0;
     pd.Sq = prev->q_len;
   }
-  size_t need = 0;
-  st = hga_stage_workspace(shape, stage_groups, &need);
-  if (st != HGA_OK) return st;
-  if (!workspace || workspace_bytes < need) return HGA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < hga_layout::stage_workspace_bytes(shape, stage_groups))
+    return HGA_ERR_WORKSPACE;
   // unions, then their sizes, then the copy sources of the union slots
-  const size_t lb = stage_list_bytes(shape->batch, shape->n_kv_heads, stage_groups);
+  const size_t lb = hga_layout::stage_list_bytes(shape->batch, shape->n_kv_heads, stage_groups);
   int32_t* ulist = (int32_t*)workspace;
   int32_t* ucount = (int32_t*)((uint8_t*)workspace + lb);
   int32_t* usrc = (int32_t*)((uint8_t*)workspace + lb +
-                             round256((size_t)shape->batch * shape->n_kv_heads * sizeof(int32_t)));
+                             hga_layout::stage_counts_bytes(shape->batch, shape->n_kv_heads));
   return from_hip(hga::launch_stage(dims_of(shape), shape->top_g > 0 ? group_idx : nullptr, K,
                                     V, K_seg, V_seg, prev ? &pd : nullptr, stage_groups,
                                     stage_capacity, K_stage, V_stage,

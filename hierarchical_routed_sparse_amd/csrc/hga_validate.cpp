@@ -1,10 +1,12 @@
 // Host-only entry points of the HGA library: shape validation, status text,
-// ABI version and the staging bound.  Plain C++ (no HIP): it is compiled into
-// libhga.so, and the CPU tests also build it on its own with the address and
-// undefined-behaviour sanitizers and drive it over many shapes.
+// ABI version, the staging bound and the workspace sizes.  Plain C++ (no HIP):
+// it is compiled into libhga.so, and the CPU tests also build it on its own
+// with the address and undefined-behaviour sanitizers and drive it over many
+// shapes.
 #include <string.h>
 
 #include "hga.h"
+#include "hga_layout.h"
 
 namespace {
 
@@ -98,6 +100,24 @@ int32_t hga_stage_min_groups(const hga_shape* shape) {
                         (shape->q_len / HGA_QBLOCK) * shape->top_g;
   const long long need = hist < sel ? hist : sel;
   return (int32_t)((need + 7) / 8 * 8);
+}
+
+hga_status hga_attend_bwd_workspace(const hga_shape* shape, size_t* bytes) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!bytes) return HGA_ERR_NULL;
+  *bytes = hga_layout::bwd_workspace_bytes(shape);
+  return HGA_OK;
+}
+
+hga_status hga_stage_workspace(const hga_shape* shape, int32_t stage_groups, size_t* bytes) {
+  hga_status st = hga_validate_shape(shape);
+  if (st != HGA_OK) return st;
+  if (!bytes) return HGA_ERR_NULL;
+  if (stage_groups < 0 || stage_groups % 8 != 0 || stage_groups > HGA_MAX_KV_LEN / 8)
+    return HGA_ERR_SHAPE;
+  *bytes = hga_layout::stage_workspace_bytes(shape, stage_groups);
+  return HGA_OK;
 }
 
 }  // extern "C"

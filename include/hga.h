@@ -298,9 +298,11 @@ hga_status hga_attend_bwd_dkdv_range(const hga_shape* shape, const void* Q, cons
  *                     (read by the prefix rule of hga_attend_fwd)
  *   K, V              [B][Hkv][C][D] dtype, the full history (C =
  *                     kv_capacity or kv_len)
- *   stage_groups      group slots of the staged history, a multiple of 8 and
- *                     at least hga_stage_min_groups(shape): the union always
- *                     fits
+ *   stage_groups      group slots of the staged history, a multiple of 8, at
+ *                     least hga_stage_min_groups(shape) (the union always
+ *                     fits) and at most HGA_MAX_KV_LEN / 8; hga_stage_workspace
+ *                     returns HGA_ERR_SHAPE for a negative value, one not a
+ *                     multiple of 8 or one above that bound
  *   stage_capacity    rows per (b, kv head) of K_stage and V_stage, a
  *                     multiple of 64, >= 8 * stage_groups + q_len
  *   K_stage, V_stage  [B][Hkv][stage_capacity][D] dtype, device memory:

@@ -1,12 +1,15 @@
-// Drives the library's host-only checks (hga_validate.cpp) over many shapes,
-// for the CPU tests' address- and undefined-behaviour-sanitized build: every
-// field takes ordinary, boundary and extreme values (seeded), and each
-// accepted shape is checked against the limits the header states.
+// Drives the library's host-only checks (hga_validate.cpp, and the workspace
+// layouts and staging checks of hga_layout.h) over many shapes, for the CPU
+// tests' address- and undefined-behaviour-sanitized build: every field takes
+// ordinary, boundary and extreme values (seeded), and each accepted shape or
+// argument set is checked against the limits the header states, with sizes
+// recomputed in 128-bit arithmetic.
 #include <climits>
 #include <cstdio>
 #include <cstring>
 
 #include "hga.h"
+#include "hga_layout.h"
 
 namespace {
 
@@ -29,6 +32,9 @@ int value() {
   return pick(1 << 20) - (1 << 10);
 }
 
+typedef unsigned __int128 u128;
+u128 up256(u128 n) { return (n + 255) / 256 * 256; }
+
 int fails = 0;
 void expect(bool ok, const char* what, const hga_shape& s) {
   if (ok) return;
@@ -41,7 +47,7 @@ void expect(bool ok, const char* what, const hga_shape& s) {
 }  // namespace
 
 int main() {
-  int accepted = 0, accepted_decode = 0;
+  int accepted = 0, accepted_decode = 0, staged = 0, staged_prev = 0;
   for (int it = 0; it < 200000; ++it) {
     hga_shape s;
     s.batch = pick(4) ? 1 + pick(16) : value();
@@ -68,6 +74,71 @@ int main() {
       expect(s.head_dim == 64 || s.head_dim == 128, "head_dim", s);
       const int g = hga_stage_min_groups(&s);
       expect(g >= 0 && g % 8 == 0 && g <= 8 * ((s.kv_len - s.q_len) / 64) + 7, "stage", s);
+      // backward workspace: the three parts, each rounded, recomputed wide
+      size_t ws = 0;
+      expect(hga_attend_bwd_workspace(&s, &ws) == HGA_OK, "bwd workspace ok", s);
+      const u128 B = (u128)s.batch, Hq = (u128)s.n_q_heads, Hkv = (u128)s.n_kv_heads;
+      const u128 want = up256(B * Hq * (u128)s.q_len * 4) +
+                        up256(B * Hq * (u128)(s.q_len / 64) * (u128)(s.kv_len / 64)) +
+                        2 * up256(B * Hkv * (u128)(s.kv_len / 64) * 4);
+      expect((u128)ws == want, "bwd workspace size", s);
+      expect(hga_attend_bwd_workspace(&s, nullptr) == HGA_ERR_NULL, "bwd workspace null", s);
+      // staging: sizes and argument checks over ordinary and extreme values
+      const int sg = pick(2) ? g + 8 * pick(64) : (pick(2) ? 8 * pick(2049) : value());
+      size_t sb = 0;
+      const hga_status sst = hga_stage_workspace(&s, sg, &sb);
+      const bool sg_ok = sg >= 0 && sg % 8 == 0 && sg <= HGA_MAX_KV_LEN / 8;
+      expect((sst == HGA_OK) == sg_ok, "stage workspace accepts", s);
+      if (sst == HGA_OK)
+        expect((u128)sb == 2 * up256(B * Hkv * (u128)sg * 4) + up256(B * Hkv * 4),
+               "stage workspace size", s);
+      const long long capw = (8LL * sg + s.q_len + 63) / 64 * 64 + 64 * pick(4);
+      const int cap = pick(2) && capw <= HGA_MAX_KV_LEN ? (int)capw
+                                                         : (pick(3) ? 64 * (pick(2049) + 1) : value());
+      hga_stage_prev pv;
+      std::memset(&pv, 0, sizeof(pv));
+      char dummy[16];
+      pv.K_stage = pick(8) ? dummy : nullptr;
+      pv.V_stage = dummy;
+      pv.workspace = dummy;
+      pv.stage_groups = pick(3) ? 8 * pick(2049) : value();
+      pv.stage_capacity = pick(3) ? 64 * (pick(2049) + 1) : value();
+      pv.q0 = pick(3) ? 64 * pick(2048) : value();
+      pv.q_len = pick(3) ? 64 * (pick(64) + 1) : value();
+      pv.workspace_bytes = pick(4) ? (size_t)pick(1 << 30) : (size_t)-1 >> pick(64);
+      const int q0s = s.kv_len - s.q_len;
+      if (pick(2) && q0s >= 64) {
+        // a consistent previous staging: an earlier segment of the history
+        pv.q_len = 64 * (1 + pick(q0s / 64 < 64 ? q0s / 64 : 64));
+        pv.q0 = 64 * pick((q0s - pv.q_len) / 64 + 1);
+        pv.stage_groups = 8 * pick(2049);
+        const long long pc = (8LL * pv.stage_groups + pv.q_len + 63) / 64 * 64 + 64 * pick(4);
+        pv.stage_capacity = pc <= HGA_MAX_KV_LEN ? (int)pc : HGA_MAX_KV_LEN;
+        const u128 need = up256((u128)s.batch * (u128)s.n_kv_heads * (u128)pv.stage_groups * 4) +
+                          up256((u128)s.batch * (u128)s.n_kv_heads * 4);
+        pv.workspace_bytes = pick(8) ? (size_t)need + (size_t)pick(512) : (size_t)need - 1;
+      }
+      const hga_stage_prev* pp = pick(2) ? &pv : nullptr;
+      const hga_status cst = hga_layout::check_stage_args(&s, sg, cap, pp);
+      if (cst == HGA_OK) {
+        ++(pp ? staged_prev : staged);
+        expect(sg % 8 == 0 && sg >= g && sg <= HGA_MAX_KV_LEN / 8, "stage groups", s);
+        expect(cap % 64 == 0 && cap <= HGA_MAX_KV_LEN && (long long)cap >= 8LL * sg + s.q_len,
+               "stage capacity", s);
+        if (pp) {
+          const long long q0 = s.kv_len - s.q_len;
+          expect(pv.K_stage && pv.V_stage && pv.workspace, "prev pointers", s);
+          expect(pv.stage_groups >= 0 && pv.stage_groups % 8 == 0 &&
+                     pv.stage_groups <= HGA_MAX_KV_LEN / 8 && pv.q0 >= 0 && pv.q0 % 64 == 0 &&
+                     pv.q_len >= 64 && pv.q_len % 64 == 0 && pv.q0 + (long long)pv.q_len <= q0 &&
+                     pv.stage_capacity % 64 == 0 && pv.stage_capacity <= HGA_MAX_KV_LEN &&
+                     (long long)pv.stage_capacity >= 8LL * pv.stage_groups + pv.q_len,
+                 "prev geometry", s);
+          expect((u128)pv.workspace_bytes >=
+                     up256(B * Hkv * (u128)pv.stage_groups * 4) + up256(B * Hkv * 4),
+                 "prev workspace", s);
+        }
+      }
     }
     hga_shape d = s;
     d.q_len = 1;
@@ -81,7 +152,14 @@ int main() {
   }
   expect(hga_validate_shape(nullptr) == HGA_ERR_NULL, "null", hga_shape{});
   expect(hga_stage_min_groups(nullptr) == -1, "null stage", hga_shape{});
-  std::printf("accepted %d block shapes and %d decode shapes; %d violations\n", accepted,
-              accepted_decode, fails);
-  return fails == 0 && accepted > 1000 && accepted_decode > 1000 ? 0 : 1;
+  size_t nb = 0;
+  expect(hga_attend_bwd_workspace(nullptr, &nb) == HGA_ERR_NULL, "null bwd workspace", hga_shape{});
+  expect(hga_stage_workspace(nullptr, 8, &nb) == HGA_ERR_NULL, "null stage workspace", hga_shape{});
+  std::printf("accepted %d block shapes, %d decode shapes, %d staging argument sets and %d "
+              "with a previous staging; %d violations\n",
+              accepted, accepted_decode, staged, staged_prev, fails);
+  return fails == 0 && accepted > 1000 && accepted_decode > 1000 && staged > 100 &&
+                 staged_prev > 100
+             ? 0
+             : 1;
 }

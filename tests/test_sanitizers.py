@@ -1,9 +1,11 @@
 """The CPU-side C++ under the address and undefined-behaviour sanitizers.
 
-- The library's host-only checks (csrc/hga_validate.cpp) are built with g++
-  and the sanitizers together with tests/sanitize_validate.cpp, which drives
-  them over 200,000 seeded shapes (ordinary, boundary and extreme field values)
-  and checks every accepted shape against the limits include/hga.h states.
+- The library's host-only checks (csrc/hga_validate.cpp, and the workspace
+  layouts and staging checks of csrc/hga_layout.h) are built with g++ and the
+  sanitizers together with tests/sanitize_validate.cpp, which drives them over
+  200,000 seeded shapes and argument sets (ordinary, boundary and extreme
+  values) and checks every accepted one against the limits include/hga.h
+  states, with the workspace sizes recomputed in 128-bit arithmetic.
 - The oracle is built with the sanitizers and the whole CPU test suite runs
   against it, with the sanitizer runtimes preloaded into the interpreter.
 Any sanitizer report aborts the run (halt_on_error), so a clean exit means no
@@ -44,6 +46,7 @@ def test_host_checks_under_sanitizers(tmp_path):
     _runtime("libasan.so")
     exe = str(tmp_path / "sanitize_validate")
     cmd = ["g++", "-std=c++17", "-O1", "-g", *SAN, "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(ROOT, "hierarchical_routed_sparse_amd", "csrc"),
            os.path.join(ROOT, "hierarchical_routed_sparse_amd", "csrc", "hga_validate.cpp"),
            os.path.join(ROOT, "tests", "sanitize_validate.cpp"), "-o", exe]
     subprocess.run(cmd, check=True)
