@@ -235,6 +235,11 @@ def test_stage_argument_errors(lib):
     r256 = lambda x: -(-x // 256) * 256
     assert n.value == 2 * r256(8 * sg * 4) + r256(8 * 4)   # unions, sizes, copy sources
     assert lib.hga_stage_workspace(ctypes.byref(s), sg + 4, ctypes.byref(n)) == 2
+    assert lib.hga_stage_workspace(ctypes.byref(s), -8, ctypes.byref(n)) == 2
+    assert lib.hga_stage_workspace(ctypes.byref(s), 131072 // 8, ctypes.byref(n)) == 0   # the bound
+    assert lib.hga_stage_workspace(ctypes.byref(s), 131072 // 8 + 8, ctypes.byref(n)) == 2
+    assert lib.hga_stage_workspace(ctypes.byref(s), sg, None) == 1
+    assert lib.hga_stage_workspace(ctypes.byref(s), sg, ctypes.byref(n)) == 0
     need = n.value
     ok = [16, 16, 16]
     stage = lambda *a: lib.hga_stage_routed(ctypes.byref(s), *a)
