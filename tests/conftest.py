@@ -21,10 +21,11 @@ def oracle():
 
 def pytest_sessionfinish(session, exitstatus):
     """Keeps the routing tie-band counts of a GPU run (how many rows a near
-    tie let differ, by stage) where the run keeps its outputs."""
+    tie let differ, by stage) as tie_band.json in the directory that
+    HGA_TEST_REPORT_DIR names, when it is set and exists."""
     gc = sys.modules.get("gpu_common")
-    out = os.path.join(ROOT, "gpurun_out")
-    if gc is None or not gc.TIE_LOG or not os.path.isdir(out):
+    out = os.environ.get("HGA_TEST_REPORT_DIR", "")
+    if gc is None or not gc.TIE_LOG or not out or not os.path.isdir(out):
         return
     import json
     with open(os.path.join(out, "tie_band.json"), "w") as f:

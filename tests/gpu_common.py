@@ -89,8 +89,8 @@ def check_routing(oracle, w, Qf, cm_o, gm_o, ci_gpu, gi_gpu, rows=None, causal=F
     return tolerated
 
 
-# per-call counts of check_routing, for the tie-band summary the full-size
-# routing test writes when a run keeps a gpurun_out/ directory
+# per-call counts of check_routing, for the tie-band summary a GPU run writes
+# when HGA_TEST_REPORT_DIR names a directory (see conftest.py)
 TIE_LOG = []
 
 
